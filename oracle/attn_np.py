@@ -1,0 +1,45 @@
+"""numpy FP64 form of the attention definition, for small shapes.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring). This is a second, independent
+evaluation of the definition: library matrix products and a library-style softmax,
+where ``attn_oracle.c`` uses explicit loops. It follows the reference of page "Audit
+SGLang interfaces and refresh validated kernel solutions",
+definitions/dense_attention/noncausal_dense_attention_h32_d{64,128}.json: scores from
+the bqhd,bkhd->bhqk contraction, times head_dim ** -0.5, softmax over keys, then the
+bhqk,bkhd->bqhd contraction with V. The prefix-cached operator
+(definitions/block_causal_attention/prefix_cached_block_causal_h32_d128.json) first
+concatenates prefix and current keys and values along the sequence axis.
+"""
+import numpy as np
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of BF16 bit patterns (uint16) to float64."""
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def softmax_last(x: np.ndarray) -> np.ndarray:
+    m = np.max(x, axis=-1, keepdims=True)
+    e = np.exp(x - m)
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def attention(q, k, v, scale=None):
+    """q [B,Nq,H,D], k/v [B,Nk,H,D] as BF16 bits or float arrays -> FP64 [B,Nq,H,D]."""
+    qf = bf16_bits_to_f64(q) if q.dtype == np.uint16 else np.asarray(q, np.float64)
+    kf = bf16_bits_to_f64(k) if k.dtype == np.uint16 else np.asarray(k, np.float64)
+    vf = bf16_bits_to_f64(v) if v.dtype == np.uint16 else np.asarray(v, np.float64)
+    D = qf.shape[-1]
+    s = D ** -0.5 if scale is None else scale
+    # [B,H,Nq,D] @ [B,H,D,Nk] -> [B,H,Nq,Nk]
+    scores = np.matmul(qf.transpose(0, 2, 1, 3), kf.transpose(0, 2, 3, 1)) * s
+    p = softmax_last(scores)
+    # [B,H,Nq,Nk] @ [B,H,Nk,D] -> [B,H,Nq,D] -> [B,Nq,H,D]
+    return np.matmul(p, vf.transpose(0, 2, 1, 3)).transpose(0, 2, 1, 3)
+
+
+def prefix_attention(q, kp, vp, kc, vc, scale=None):
+    """Keys cat(kp, kc) and values cat(vp, vc) along the sequence axis."""
+    return attention(q, np.concatenate([kp, kc], axis=1), np.concatenate([vp, vc], axis=1),
+                     scale=scale)

@@ -1,0 +1,141 @@
+/*
+ * FP64 CPU oracle for dense noncausal attention and its prefix-cached variant.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may link, load or call
+ * this file; only the tests, the smoke check and the CPU-baseline leg of the
+ * benchmark use it. It shares no code with the HIP library.
+ *
+ * What it computes (page "Audit SGLang interfaces and refresh validated kernel
+ * solutions"):
+ *   - definitions/dense_attention/noncausal_dense_attention_h32_d128.json and
+ *     ..._h32_d64.json, field "reference": scores = einsum(bqhd,bkhd->bhqk) of Q and
+ *     K in float, times head_dim ** -0.5; probabilities = softmax over k;
+ *     output = einsum(bhqk,bkhd->bqhd) of the probabilities and V.
+ *   - definitions/block_causal_attention/prefix_cached_block_causal_h32_d128.json,
+ *     field "reference" (post-change text): keys and values are the concatenation
+ *     along the sequence axis of (K_prefix, K_current) and (V_prefix, V_current);
+ *     every query sees every key; scale 128 ** -0.5.
+ * The pages evaluate in FP32; this oracle evaluates the same formula in FP64 and
+ * returns the unrounded FP64 result (the pages' final BF16 cast is left to the
+ * comparison).
+ *
+ * Tensors are [B, N, H, D], contiguous, holding BF16 bit patterns (uint16).
+ * Widening BF16 to FP64 is exact: the 16 bits are the top half of an FP32.
+ *
+ * The key sequence is the concatenation of segment 0 (n0 rows, e.g. the prefix)
+ * and segment 1 (n1 rows, e.g. the current keys). Dense attention is n1 == 0.
+ *
+ * Softmax is evaluated row by row as exp(s_j - max_j s_j) / sum_j exp(s_j - max_j s_j),
+ * which is the softmax of the row (the subtracted maximum cancels exactly).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+static double bf16_to_f64(uint16_t bits) {
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* Pointer to element [b, j, h, 0] of the concatenated key (or value) sequence. */
+static const uint16_t* seq_row(const uint16_t* s0, long n0, const uint16_t* s1, long n1,
+                               long b, long j, long H, long D, long h) {
+    if (j < n0) return s0 + ((b * n0 + j) * H + h) * D;
+    return s1 + ((b * n1 + (j - n0)) * H + h) * D;
+}
+
+/*
+ * Computes output rows of attention in FP64.
+ *
+ * rows: flat indices r = (b * Nq + i) * H + h into the [B, Nq, H] row space, or
+ *       NULL for every row in order. nrows: how many.
+ * out:  [nrows, D] FP64 outputs (unrounded).
+ * lse:  optional [nrows] natural-log log-sum-exp of the scaled scores.
+ * psum: optional [nrows] sum of the normalised probabilities (should be 1).
+ * scale_override: <= 0 means head_dim ** -0.5, the pages' fixed scale.
+ * Returns 0, -1 on bad arguments, -2 on a row index out of range, -3 on allocation
+ * failure.
+ */
+int oracle_attn_rows(const uint16_t* q, const uint16_t* k0, const uint16_t* v0, long n0,
+                     const uint16_t* k1, const uint16_t* v1, long n1, long B, long Nq,
+                     long H, long D, const long* rows, long nrows, double* out, double* lse,
+                     double* psum, double scale_override) {
+    if (!q || !out || B < 1 || Nq < 1 || H < 1 || D < 1 || n0 < 0 || n1 < 0) return -1;
+    if (n0 + n1 < 1) return -1;
+    if (n0 > 0 && (!k0 || !v0)) return -1;
+    if (n1 > 0 && (!k1 || !v1)) return -1;
+    const long nk = n0 + n1;
+    const long total = B * Nq * H;
+    if (!rows) nrows = total;
+    const double scale = scale_override > 0 ? scale_override : pow((double)D, -0.5);
+    int fail = 0;
+
+#pragma omp parallel
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)nk);
+        double* qd = (double*)malloc(sizeof(double) * (size_t)D);
+        if (!s || !qd) {
+#pragma omp atomic write
+            fail = 3;
+        } else {
+#pragma omp for schedule(dynamic, 16)
+            for (long t = 0; t < nrows; ++t) {
+                const long r = rows ? rows[t] : t;
+                if (r < 0 || r >= total) {
+#pragma omp atomic write
+                    fail = 2;
+                    continue;
+                }
+                const long h = r % H;
+                const long bi = r / H;
+                const long i = bi % Nq;
+                const long b = bi / Nq;
+                const uint16_t* qr = q + ((b * Nq + i) * H + h) * D;
+                for (long d = 0; d < D; ++d) qd[d] = bf16_to_f64(qr[d]);
+
+                /* scores s_j = scale * <q_i, k_j> over the concatenated keys */
+                double mx = -INFINITY;
+                for (long j = 0; j < nk; ++j) {
+                    const uint16_t* kr = seq_row(k0, n0, k1, n1, b, j, H, D, h);
+                    double dot = 0.0;
+                    for (long d = 0; d < D; ++d) dot += qd[d] * bf16_to_f64(kr[d]);
+                    s[j] = dot * scale;
+                    if (s[j] > mx) mx = s[j];
+                }
+                /* softmax: e_j = exp(s_j - max), l = sum e_j, p_j = e_j / l */
+                double l = 0.0;
+                for (long j = 0; j < nk; ++j) {
+                    s[j] = exp(s[j] - mx);
+                    l += s[j];
+                }
+                double* o = out + t * D;
+                for (long d = 0; d < D; ++d) o[d] = 0.0;
+                double ps = 0.0;
+                for (long j = 0; j < nk; ++j) {
+                    const double p = s[j] / l;
+                    ps += p;
+                    const uint16_t* vr = seq_row(v0, n0, v1, n1, b, j, H, D, h);
+                    for (long d = 0; d < D; ++d) o[d] += p * bf16_to_f64(vr[d]);
+                }
+                if (lse) lse[t] = mx + log(l);
+                if (psum) psum[t] = ps;
+            }
+        }
+        free(s);
+        free(qd);
+    }
+    return fail ? -fail : 0;
+}
+
+/* Number of OpenMP threads the oracle will use (1 when built without OpenMP). */
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    extern int omp_get_max_threads(void);
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

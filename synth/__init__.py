@@ -1,0 +1,179 @@
+"""Seeded synthetic inputs for the attention workloads.
+
+This module holds input generation and workload bookkeeping only (shapes, seeds,
+FLOP and byte counts). It contains none of the attention arithmetic, so both the
+FP64 oracle and the HIP library can be fed from it without sharing any code.
+
+The pages measure on captured serving activations (page "Audit SGLang interfaces
+and refresh validated kernel solutions", README "Task acceptance configs" and the
+dataset description) that are not available here; these seeded inputs stand in for
+them, keeping the operators' shapes (H = 32, D in {64, 128}, layout [B, N, H, D],
+prefix operand order Q, K_prefix, V_prefix, K_current, V_current) and the BF16 type.
+
+Generator: numpy ``Generator(PCG64(seed))``, ``standard_normal(dtype=float32)``
+times sigma, rounded to BF16 with round-to-nearest-even on the FP32 bit pattern.
+Seeds are ``1000 * (k + 1) + t`` for workload index k and tensor index t in call
+order (dense: Q=0, K=1, V=2; prefix: Q=0, K_prefix=1, V_prefix=2, K_current=3,
+V_current=4), so every tensor is reproducible on its own.
+"""
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional, Tuple
+
+import numpy as np
+
+H_PAGES = 32  # the pages fix H = 32 for every attention definition
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round FP32 values to BF16 (round to nearest, ties to even); returns uint16 bits.
+
+    NaN inputs are not expected from the generator and are not special-cased.
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of BF16 bits to FP32 (for inspection and input statistics)."""
+    return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def normal_bf16(shape, seed: int, sigma: float = 1.0) -> np.ndarray:
+    """BF16 bits of iid N(0, sigma^2) draws from PCG64(seed)."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    x = g.standard_normal(size=shape, dtype=np.float32)
+    if sigma != 1.0:
+        x *= np.float32(sigma)
+    return f32_to_bf16_bits(x)
+
+
+def outlier_channels(seed: int, H: int, D: int, count: int = 4) -> np.ndarray:
+    """[H, count] distinct channel indices per head, drawn from PCG64(seed)."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    return np.stack([np.sort(g.choice(D, size=count, replace=False)) for _ in range(H)])
+
+
+def normal_bf16_outliers(shape, seed: int, sigma: float, channels: np.ndarray,
+                         factor: float) -> np.ndarray:
+    """N(0, sigma^2) draws with the given per-head channels multiplied by ``factor``
+    before rounding to BF16. shape is [B, N, H, D]; channels is [H, count]."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    x = g.standard_normal(size=shape, dtype=np.float32)
+    x *= np.float32(sigma)
+    H = shape[2]
+    for h in range(H):
+        x[:, :, h, channels[h]] *= np.float32(factor)
+    return f32_to_bf16_bits(x)
+
+
+@dataclass
+class Workload:
+    """One synthetic attention workload.
+
+    kind "dense": Q [B,Nq,H,D], K/V [B,Nk,H,D] (Nk == Nq for self attention).
+    kind "prefix": Q [B,Nq,H,D], K/V_prefix [B,Np,H,D], K/V_current [B,Nq,H,D].
+    """
+    name: str
+    kind: str
+    B: int
+    Nq: int
+    H: int
+    D: int
+    index: int            # workload index k used in the seeds
+    Nk: int = 0           # dense: key count (defaults to Nq)
+    Np: int = 0           # prefix: prefix length
+    sigma_qk: float = 1.0
+    outliers: int = 0     # channels per head scaled by outlier_factor in Q and K
+    outlier_factor: float = 8.0
+    description: str = ""
+    extra: Dict = field(default_factory=dict)
+
+    def __post_init__(self):
+        if self.kind == "dense" and self.Nk == 0:
+            self.Nk = self.Nq
+
+    @property
+    def keys(self) -> int:
+        return self.Np + self.Nq if self.kind == "prefix" else self.Nk
+
+    @property
+    def flop(self) -> int:
+        """4*B*H*Nq*Nk*D: the two contractions (QK^T and PV), 2 FLOP per multiply-add."""
+        return 4 * self.B * self.H * self.Nq * self.keys * self.D
+
+    @property
+    def exps(self) -> int:
+        return self.B * self.H * self.Nq * self.keys
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        """Every input read once and the output written once, 2 bytes per element."""
+        q = self.B * self.Nq * self.H * self.D
+        kv = 2 * self.B * self.keys * self.H * self.D
+        return 2 * (q + kv + q)
+
+    def seed(self, t: int) -> int:
+        return 1000 * (self.index + 1) + t
+
+    def tensors(self) -> Tuple[np.ndarray, ...]:
+        """BF16 bit arrays in call order: (Q, K, V) or (Q, Kp, Vp, Kc, Vc)."""
+        B, Nq, H, D = self.B, self.Nq, self.H, self.D
+        if self.kind == "dense":
+            shapes = [(B, Nq, H, D), (B, self.Nk, H, D), (B, self.Nk, H, D)]
+            qk = {0, 1}
+        else:
+            shapes = [(B, Nq, H, D), (B, self.Np, H, D), (B, self.Np, H, D),
+                      (B, Nq, H, D), (B, Nq, H, D)]
+            qk = {0, 1, 3}
+        chans = None
+        if self.outliers:
+            chans = outlier_channels(1000 * (self.index + 1) + 99, H, D, self.outliers)
+        out = []
+        for t, shp in enumerate(shapes):
+            if t in qk and chans is not None:
+                out.append(normal_bf16_outliers(shp, self.seed(t), self.sigma_qk, chans,
+                                                self.outlier_factor))
+            elif t in qk:
+                out.append(normal_bf16(shp, self.seed(t), self.sigma_qk))
+            else:
+                out.append(normal_bf16(shp, self.seed(t), 1.0))
+        return tuple(out)
+
+
+# The six workloads. Index k feeds the seeds; k = 0..5.
+WORKLOADS: List[Workload] = [
+    Workload("dense_b1_n256_h32_d64", "dense", 1, 256, 32, 64, 0,
+             description="Dense noncausal MHA, B=1 N=256 H=32 D=64, N(0,1), scale 1/8"),
+    Workload("dense_b1_n4096_h32_d128", "dense", 1, 4096, 32, 128, 1,
+             description="Dense noncausal MHA, B=1 N=4096 H=32 D=128, N(0,1), "
+                         "scale 1/sqrt(128)"),
+    Workload("dense_b2_n16384_h32_d64", "dense", 2, 16384, 32, 64, 2,
+             description="Dense noncausal MHA long sequence, B=2 N=16384 H=32 D=64, "
+                         "N(0,1), scale 1/8"),
+    Workload("prefix_b1_nq4096_np1024_h32_d128", "prefix", 1, 4096, 32, 128, 3, Np=1024,
+             description="Prefix-cached attention, Q [1,4096,32,128], K/V prefix "
+                         "[1,1024,32,128], K/V current [1,4096,32,128], 5120 keys, "
+                         "scale 1/sqrt(128)"),
+    Workload("dense_b1024_n64_h32_d64", "dense", 1024, 64, 32, 64, 4,
+             description="Many short sequences, B=1024 N=64 H=32 D=64, N(0,1)"),
+    Workload("dense_b8_n1999_h32_d128_outliers", "dense", 8, 1999, 32, 128, 5,
+             sigma_qk=3.0, outliers=4, outlier_factor=8.0,
+             description="Ragged stress, B=8 N=1999 H=32 D=128, Q,K ~ N(0,3^2) with 4 "
+                         "outlier channels per head (same in Q and K) scaled x8, V ~ N(0,1)"),
+]
+
+BY_NAME = {w.name: w for w in WORKLOADS}
+
+
+def workload(name_or_index) -> Workload:
+    if isinstance(name_or_index, int):
+        return WORKLOADS[name_or_index]
+    return BY_NAME[name_or_index]
+
+
+def small(kind: str, B: int, Nq: int, H: int, D: int, seed_base: int, Nk: Optional[int] = None,
+          Np: int = 0, sigma_qk: float = 1.0) -> Workload:
+    """An ad-hoc seeded workload (tests); seed_base plays the role of the index k."""
+    return Workload(f"{kind}_b{B}_nq{Nq}_h{H}_d{D}_s{seed_base}", kind, B, Nq, H, D,
+                    seed_base, Nk=Nk or 0, Np=Np, sigma_qk=sigma_qk)

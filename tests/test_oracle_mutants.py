@@ -1,0 +1,71 @@
+"""Mutation check of the oracle's pins, on the CPU.
+
+Each case plants one plausible mistake in a copy of oracle/attn_oracle.c, builds it
+into a temporary library and runs the pin suite (tests/test_oracle.py) against it in
+a subprocess. Every mutant must make at least one pin fail; the unmodified source
+must pass. This shows the pins constrain the oracle rather than restate it.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "attn_oracle.c")
+
+MUTANTS = {
+    "scale_dropped": ("s[j] = dot * scale;", "s[j] = dot;"),
+    "scale_inverse_d": ("pow((double)D, -0.5)", "(1.0 / (double)D)"),
+    "exponent_sign": ("s[j] = exp(s[j] - mx);", "s[j] = exp(mx - s[j]);"),
+    "max_not_subtracted": ("s[j] = exp(s[j] - mx);", "s[j] = exp(s[j]);"),
+    "not_normalised": ("const double p = s[j] / l;", "const double p = s[j];"),
+    "key_layout_bhnd": ("if (j < n0) return s0 + ((b * n0 + j) * H + h) * D;",
+                        "if (j < n0) return s0 + ((b * H + h) * n0 + j) * D;"),
+    "query_head_index_swapped": ("const long h = r % H;\n                const long bi = r / H;\n"
+                                 "                const long i = bi % Nq;\n"
+                                 "                const long b = bi / Nq;",
+                                 "const long i = r % Nq;\n                const long bi = r / Nq;\n"
+                                 "                const long h = bi % H;\n"
+                                 "                const long b = bi / H;"),
+    "segments_swapped": ("if (j < n0) return s0 + ((b * n0 + j) * H + h) * D;\n"
+                         "    return s1 + ((b * n1 + (j - n0)) * H + h) * D;",
+                         "if (j < n1) return s1 + ((b * n1 + j) * H + h) * D;\n"
+                         "    return s0 + ((b * n0 + (j - n1)) * H + h) * D;"),
+    "values_read_from_keys": ("seq_row(v0, n0, v1, n1, b, j, H, D, h)",
+                              "seq_row(k0, n0, k1, n1, b, j, H, D, h)"),
+    "last_key_dropped": ("for (long j = 0; j < nk; ++j) {\n                    const uint16_t* kr",
+                         "for (long j = 0; j < nk - 1; ++j) {\n                    const uint16_t* kr"),
+}
+
+
+def _build_variant(tmp_path, name, src_text):
+    c = tmp_path / f"{name}.c"
+    so = tmp_path / f"lib{name}.so"
+    c.write_text(src_text)
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-o", str(so),
+                    str(c), "-lm"], check=True)
+    return str(so)
+
+
+def _run_pins(lib):
+    env = dict(os.environ, ORACLE_LIB=lib, OMP_NUM_THREADS="2")
+    return subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                           os.path.join(ROOT, "tests", "test_oracle.py")],
+                          cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
+
+
+def test_unmodified_oracle_passes_pins(tmp_path):
+    lib = _build_variant(tmp_path, "clean", open(SRC).read())
+    r = _run_pins(lib)
+    assert r.returncode == 0, r.stdout[-2000:]
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_fails_some_pin(tmp_path, name):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    lib = _build_variant(tmp_path, name, src.replace(old, new))
+    r = _run_pins(lib)
+    assert r.returncode != 0, f"mutant {name} passed every pin:\n{r.stdout[-2000:]}"
