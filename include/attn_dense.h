@@ -1,0 +1,123 @@
+/*
+ * attn_dense.h - C ABI of the MI355X (gfx950) dense attention library.
+ *
+ * Operations (page "Audit SGLang interfaces and refresh validated kernel solutions"):
+ *   - definitions/dense_attention/noncausal_dense_attention_h32_d128.json and
+ *     ..._h32_d64.json: O = softmax(Q K^T * D^-0.5) V per batch and head, noncausal,
+ *     no mask, no dropout, FP32 accumulation, BF16 output. Self attention has Nq = Nk;
+ *     the description also admits cross attention with Nq != Nk.
+ *   - definitions/block_causal_attention/prefix_cached_block_causal_h32_d128.json
+ *     (post-change text): each query attends to every key of the concatenation of
+ *     K_prefix then K_current along the sequence axis, with V_prefix then V_current.
+ *     The operand order Q, K_prefix, V_prefix, K_current, V_current is the pages'
+ *     positional order (same page, interfaces.json entry for that definition).
+ * The scale is not an argument: the pages fix it to head_dim ** -0.5 (same page,
+ * README "Feasible changes" and the definitions' descriptions).
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors are contiguous [B, N, H, D] arrays of BF16 (raw 16-bit patterns) in
+ *     device memory of the current HIP device. N is Nq for Q and the output, Nk / Np /
+ *     Nq for the key and value operands as stated per call.
+ *   - Every pointer must be 16-byte aligned (the kernels use 128-bit accesses).
+ *   - D must be 64 or 128. H, B and the sequence lengths must be >= 1 (Np >= 0).
+ *     The pages fix H = 32; any H >= 1 is accepted.
+ *   - Ownership: the caller owns all buffers. Inputs are read only and never written.
+ *     The output is caller-allocated and must not overlap any input.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL means the null stream) and the
+ *     call returns without waiting. Device-side faults surface at the caller's next
+ *     synchronisation. Results are deterministic: the same inputs and the same launch
+ *     plan give the same bits.
+ *   - Return value: ATTN_OK (0) or a negative ATTN_ERR_* code. All argument checks run
+ *     before any HIP call, so an invalid call touches no device state. No exception
+ *     crosses the ABI.
+ *   - Split-KV work space (used when the grid would underfill the GPU) is owned by the
+ *     library: one buffer per device, grown on demand and kept until process exit.
+ *     Growing it synchronises the device; callers that capture HIP graphs reserve it
+ *     first with attn_reserve_workspace() or one uncaptured call of the same shape.
+ */
+#ifndef ATTN_DENSE_H
+#define ATTN_DENSE_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_OK 0
+#define ATTN_ERR_NULL (-1)        /* a required pointer is NULL */
+#define ATTN_ERR_SHAPE (-2)       /* B, N, H < 1, or Np < 0 */
+#define ATTN_ERR_UNSUPPORTED (-3) /* D not in {64, 128}, or a bad launch option */
+#define ATTN_ERR_ALIGN (-4)       /* a pointer is not 16-byte aligned */
+#define ATTN_ERR_ALIAS (-5)       /* the output overlaps an input */
+#define ATTN_ERR_OVERFLOW (-6)    /* a size exceeds the index range of the kernels */
+#define ATTN_ERR_WORKSPACE (-7)   /* the split-KV work space could not be allocated */
+#define ATTN_ERR_HIP (-8)         /* a HIP runtime call or kernel launch failed */
+
+/*
+ * Dense noncausal self attention (Nq = Nk = N).
+ * q, k, v: [B, N, H, D] BF16 inputs. out: [B, N, H, D] BF16 output.
+ * stream: hipStream_t to enqueue on.
+ */
+int attn_dense(const void* q, const void* k, const void* v, void* out, int B, int N, int H,
+               int D, void* stream);
+
+/*
+ * Prefix-cached attention: Q attends to every key of (K_prefix ++ K_current).
+ * q: [B, Nq, H, D]; kp, vp: [B, Np, H, D]; kc, vc: [B, Nq, H, D]; out: [B, Nq, H, D].
+ * The pages require Np >= 1; Np = 0 is also accepted and equals
+ * attn_dense(q, kc, vc) (kp and vp may then be NULL).
+ */
+int attn_prefix(const void* q, const void* kp, const void* vp, const void* kc, const void* vc,
+                void* out, int B, int Nq, int Np, int H, int D, void* stream);
+
+/*
+ * Dense noncausal cross attention (Nq != Nk allowed by the definitions' description).
+ * q: [B, Nq, H, D]; k, v: [B, Nk, H, D]; out: [B, Nq, H, D].
+ */
+int attn_cross(const void* q, const void* k, const void* v, void* out, int B, int Nq, int Nk,
+               int H, int D, void* stream);
+
+/*
+ * General form behind the three calls above, with explicit launch options.
+ * The keys are segment 0 (k0/v0, n0 rows) followed by segment 1 (k1/v1, n1 rows);
+ * n0 + n1 >= 1, and a segment with zero rows may have NULL pointers.
+ * num_splits: 0 = automatic, otherwise the number of key ranges computed in parallel
+ *             and merged by a combine step (clamped to the number of key tiles).
+ * waves:      0 = automatic, otherwise 2 or 4 wavefronts (32 query rows each) per
+ *             workgroup.
+ * Results for any options agree with each other up to floating-point rounding.
+ */
+int attn_fwd_ex(const void* q, const void* k0, const void* v0, int n0, const void* k1,
+                const void* v1, int n1, void* out, int B, int Nq, int H, int D, int num_splits,
+                int waves, void* stream);
+
+/*
+ * Launch plan the library would use for a call, computed on the host only (no HIP
+ * call). Any output pointer may be NULL. Returns ATTN_OK or a shape/size error.
+ *   splits:          key ranges computed in parallel (1 = no combine step)
+ *   waves:           wavefronts per workgroup
+ *   workgroups:      workgroups of the main kernel
+ *   workspace_bytes: split-KV work space needed (0 when splits == 1)
+ */
+int attn_plan(int B, int Nq, int Nk, int H, int D, int num_splits, int waves, int* splits,
+              int* waves_out, long long* workgroups, long long* workspace_bytes);
+
+/*
+ * Makes sure the current device's split-KV work space holds at least `bytes`
+ * (allocating and synchronising the device if it must grow). Returns ATTN_OK,
+ * ATTN_ERR_WORKSPACE or ATTN_ERR_HIP.
+ */
+int attn_reserve_workspace(long long bytes);
+
+/* Static description of an error code (never NULL). */
+const char* attn_strerror(int code);
+
+/* ABI version of this header: 1. */
+int attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_DENSE_H */

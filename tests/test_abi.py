@@ -1,0 +1,125 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol the header
+declares, and rejects invalid arguments before any HIP call (pointer values here are
+never dereferenced)."""
+import os
+import re
+
+import pytest
+
+import transformer_attention_dense_amd as attn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_dense.h")
+
+A = 0x7F0000000000  # fake, 16-byte aligned device addresses; never dereferenced
+MB = 1 << 20
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(attn_\w+)\s*\(", text, flags=re.M)
+
+
+def test_header_declares_the_abi_and_library_exports_it():
+    names = declared_functions()
+    assert set(names) == set(attn.SYMBOLS), names
+    lib = attn.library()
+    for n in names:
+        assert hasattr(lib, n), f"missing export {n}"
+
+
+def test_error_codes_match_header():
+    text = open(HEADER).read()
+    codes = dict((int(v), k) for k, v in re.findall(r"#define (ATTN_ERR_\w+) \((-\d+)\)", text))
+    assert codes == attn.ERRORS
+    for c in list(codes) + [0, -99]:
+        assert isinstance(attn.attn_strerror(c), str) and attn.attn_strerror(c)
+
+
+def test_abi_version():
+    assert attn.attn_abi_version() == 1
+
+
+def dense_call(q=A, k=A + 64 * MB, v=A + 128 * MB, out=A + 192 * MB, B=1, N=256, H=32, D=64):
+    return attn.attn_dense(q, k, v, out, B, N, H, D, None)
+
+
+def test_null_pointers_rejected():
+    assert dense_call(q=None) == -1
+    assert dense_call(k=None) == -1
+    assert dense_call(v=None) == -1
+    assert dense_call(out=None) == -1
+    assert attn.attn_prefix(A, None, None, None, A + MB, A + 2 * MB, 1, 4, 0, 1, 64, None) == -1
+    assert attn.attn_prefix(A, None, A + MB, A + 2 * MB, A + 3 * MB, A + 4 * MB, 1, 4, 2, 1, 64,
+                            None) == -1
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(N=0), dict(H=0), dict(B=-1), dict(N=-5)])
+def test_bad_shapes_rejected(kw):
+    assert dense_call(**kw) == -2
+
+
+def test_prefix_negative_prefix_rejected():
+    assert attn.attn_prefix(A, A + MB, A + 2 * MB, A + 3 * MB, A + 4 * MB, A + 5 * MB,
+                            1, 4, -1, 1, 64, None) == -2
+
+
+@pytest.mark.parametrize("D", [0, 32, 96, 256, 65])
+def test_unsupported_head_dim_rejected(D):
+    assert dense_call(D=D) == -3
+
+
+def test_bad_launch_options_rejected():
+    assert attn.attn_fwd_ex(A, A + MB, A + 2 * MB, 4, None, None, 0, A + 3 * MB, 1, 4, 1, 64,
+                            -1, 0, None) == -3
+    assert attn.attn_fwd_ex(A, A + MB, A + 2 * MB, 4, None, None, 0, A + 3 * MB, 1, 4, 1, 64,
+                            0, 3, None) == -3
+
+
+def test_misaligned_pointers_rejected():
+    assert dense_call(q=A + 2) == -4
+    assert dense_call(k=A + 64 * MB + 8) == -4
+    assert dense_call(out=A + 192 * MB + 1) == -4
+
+
+def test_output_overlapping_an_input_rejected():
+    # q, k, v each 1*256*32*64*2 = 1 MiB
+    assert dense_call(out=A) == -5
+    assert dense_call(out=A + 64 * MB - 512 * 1024) == -5
+    assert dense_call(out=A + 128 * MB + 16) == -5
+    # adjacent but not overlapping is fine as far as validation goes
+    assert attn.attn_plan(1, 256, 256, 32, 64)["splits"] >= 1
+
+
+def test_sizes_beyond_index_range_rejected():
+    assert dense_call(N=1 << 20, H=32, D=128) == -6
+    with pytest.raises(attn.AttnError):
+        attn.attn_plan(1, 1 << 20, 16, 32, 128)
+
+
+def test_plan_for_the_workloads():
+    p1 = attn.attn_plan(1, 4096, 4096, 32, 128)
+    assert p1["splits"] == 1 and p1["waves"] == 4 and p1["workgroups"] == 32 * 32
+    assert p1["workspace_bytes"] == 0
+    p3 = attn.attn_plan(1, 4096, 5120, 32, 128)
+    assert p3["splits"] == 1 and p3["workgroups"] == 1024
+    # few query blocks and long keys -> the keys are split and a work space is needed
+    ps = attn.attn_plan(1, 64, 8192, 2, 128)
+    assert ps["splits"] > 1 and ps["workspace_bytes"] > 0
+    # explicit split counts are clamped to the number of key tiles, with no empty split
+    pe = attn.attn_plan(1, 100, 130, 1, 64, num_splits=16)
+    assert pe["splits"] == 3
+    pe = attn.attn_plan(1, 100, 1999, 1, 64, num_splits=7)
+    tiles = -(-1999 // 64)
+    per = -(-tiles // 7)
+    assert pe["splits"] == -(-tiles // per)
+
+
+def test_python_helpers_validate_before_the_library():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 4, 1, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        attn.dense(x, x, x)  # CPU tensors are rejected
+    with pytest.raises(TypeError):
+        attn.dense(x.float(), x, x)

@@ -1,0 +1,253 @@
+// C ABI of the dense attention library: argument validation, launch planning,
+// split-KV work-space ownership and kernel dispatch. Declared in include/attn_dense.h.
+//
+// Every check runs before the first HIP call, so invalid arguments are reported
+// without touching the device.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include <mutex>
+
+#include "attn_dense.h"
+#include "attn_launch.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+constexpr long long kIndexLimit = (1LL << 31) - 1;
+
+struct Workspace {
+    void* ptr = nullptr;
+    size_t bytes = 0;
+};
+
+std::mutex g_ws_mutex;
+Workspace g_ws[kMaxDevices];
+
+struct Plan {
+    int splits;
+    int waves;
+    int m_blocks;
+    int keys_per_split;
+    long long workgroups;
+    long long workspace_bytes;
+};
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+bool overlaps(const void* a, long long abytes, const void* b, long long bbytes) {
+    if (!a || !b || abytes <= 0 || bbytes <= 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a);
+    const uintptr_t b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+
+// Sizes and launch shape. Returns ATTN_OK or an error code.
+int make_plan(int B, int Nq, int Nk, int H, int D, int num_splits, int waves, Plan* out) {
+    if (B < 1 || Nq < 1 || Nk < 1 || H < 1) return ATTN_ERR_SHAPE;
+    if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+    if (num_splits < 0 || (waves != 0 && waves != 2 && waves != 4)) return ATTN_ERR_UNSUPPORTED;
+    // Offsets inside one batch of a tensor are formed in 32 bits before widening.
+    if ((long long)Nq * H * D > kIndexLimit || (long long)Nk * H * D > kIndexLimit)
+        return ATTN_ERR_OVERFLOW;
+    if ((long long)B * H > kIndexLimit || (long long)B * Nq > kIndexLimit ||
+        (long long)B * Nk > kIndexLimit)
+        return ATTN_ERR_OVERFLOW;
+
+    const int tile = attn::kKeyTile;
+    const int key_tiles = (Nk + tile - 1) / tile;
+    int w = waves;
+    if (w == 0) w = (Nq <= 64) ? 2 : 4;
+    const int bm = 32 * w;
+    const long long m_blocks = (Nq + bm - 1) / bm;
+    const long long base = m_blocks * B * H;
+
+    int s = num_splits;
+    if (s == 0) {
+        // Split the keys only when the grid underfills the GPU (256 CUs, two
+        // workgroups each) and every split keeps at least four key tiles.
+        const long long target = 512;
+        s = 1;
+        while (base * s * 2 <= target && key_tiles / (s * 2) >= 4) s *= 2;
+    }
+    if (s > key_tiles) s = key_tiles;
+    if (s < 1) s = 1;
+    const int tiles_per_split = (key_tiles + s - 1) / s;
+    s = (key_tiles + tiles_per_split - 1) / tiles_per_split;  // no empty split
+
+    const long long wg = base * s;
+    if (wg > kIndexLimit) return ATTN_ERR_OVERFLOW;
+    out->splits = s;
+    out->waves = w;
+    out->m_blocks = (int)m_blocks;
+    out->keys_per_split = tiles_per_split * tile;
+    out->workgroups = wg;
+    const long long rows = (long long)B * Nq * H;
+    out->workspace_bytes = (s > 1) ? (long long)s * rows * (D + 1) * 4 + 256 : 0;
+    return ATTN_OK;
+}
+
+int reserve(long long bytes, void** ptr_out) {
+    if (bytes <= 0) {
+        if (ptr_out) *ptr_out = nullptr;
+        return ATTN_OK;
+    }
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return ATTN_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return ATTN_ERR_WORKSPACE;
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    Workspace& ws = g_ws[dev];
+    if (ws.bytes < (size_t)bytes) {
+        if (getenv("ATTN_TEST_FAIL_ALLOC")) return ATTN_ERR_WORKSPACE;
+        if (ws.ptr) {
+            // Earlier launches may still read the old buffer.
+            if (hipDeviceSynchronize() != hipSuccess) return ATTN_ERR_HIP;
+            (void)hipFree(ws.ptr);
+            ws.ptr = nullptr;
+            ws.bytes = 0;
+        }
+        void* p = nullptr;
+        if (hipMalloc(&p, (size_t)bytes) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return ATTN_ERR_WORKSPACE;
+        }
+        ws.ptr = p;
+        ws.bytes = (size_t)bytes;
+    }
+    if (ptr_out) *ptr_out = ws.ptr;
+    return ATTN_OK;
+}
+
+int run(const void* q, const void* k0, const void* v0, int n0, const void* k1, const void* v1,
+        int n1, void* out, int B, int Nq, int H, int D, int num_splits, int waves,
+        void* stream) {
+    if (!q || !out) return ATTN_ERR_NULL;
+    if (n0 < 0 || n1 < 0) return ATTN_ERR_SHAPE;
+    if (n0 > 0 && (!k0 || !v0)) return ATTN_ERR_NULL;
+    if (n1 > 0 && (!k1 || !v1)) return ATTN_ERR_NULL;
+    if ((long long)n0 + n1 > kIndexLimit) return ATTN_ERR_OVERFLOW;
+    const int nk = n0 + n1;
+    Plan plan;
+    const int rc = make_plan(B, Nq, nk, H, D, num_splits, waves, &plan);
+    if (rc != ATTN_OK) return rc;
+    if (misaligned(q) || misaligned(out) || (n0 && (misaligned(k0) || misaligned(v0))) ||
+        (n1 && (misaligned(k1) || misaligned(v1))))
+        return ATTN_ERR_ALIGN;
+    const long long qbytes = 2LL * B * Nq * H * D;
+    const long long s0 = 2LL * B * n0 * H * D;
+    const long long s1 = 2LL * B * n1 * H * D;
+    if (overlaps(out, qbytes, q, qbytes) || overlaps(out, qbytes, k0, s0) ||
+        overlaps(out, qbytes, v0, s0) || overlaps(out, qbytes, k1, s1) ||
+        overlaps(out, qbytes, v1, s1))
+        return ATTN_ERR_ALIAS;
+
+    // ---- device work from here on
+    void* ws = nullptr;
+    if (plan.splits > 1) {
+        const int wrc = reserve(plan.workspace_bytes, &ws);
+        if (wrc != ATTN_OK) return wrc;
+    }
+    const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    attn::FwdParams p;
+    p.q = static_cast<const uint16_t*>(q);
+    p.k0 = static_cast<const uint16_t*>(n0 ? k0 : k1);
+    p.v0 = static_cast<const uint16_t*>(n0 ? v0 : v1);
+    p.k1 = static_cast<const uint16_t*>(n0 ? k1 : nullptr);
+    p.v1 = static_cast<const uint16_t*>(n0 ? v1 : nullptr);
+    p.n0 = n0 ? n0 : n1;
+    p.n1 = n0 ? n1 : 0;
+    p.out = static_cast<uint16_t*>(out);
+    const long long rows = (long long)B * Nq * H;
+    p.part_o = nullptr;
+    p.part_lse = nullptr;
+    if (plan.splits > 1) {
+        p.part_lse = static_cast<float*>(ws);
+        const long long lse_bytes = ((long long)plan.splits * rows * 4 + 255) & ~255LL;
+        p.part_o = reinterpret_cast<float*>(static_cast<char*>(ws) + lse_bytes);
+    }
+    p.B = B;
+    p.Nq = Nq;
+    p.H = H;
+    p.keys_per_split = plan.keys_per_split;
+    p.splits = plan.splits;
+    p.m_blocks = plan.m_blocks;
+    p.c = (float)(pow((double)D, -0.5) * 1.4426950408889634);  // D^-0.5 * log2(e)
+
+    if (attn::launch_fwd(D, plan.waves, p, plan.workgroups, st) != hipSuccess)
+        return ATTN_ERR_HIP;
+    if (plan.splits > 1) {
+        attn::CombineParams cp;
+        cp.part_o = p.part_o;
+        cp.part_lse = p.part_lse;
+        cp.out = p.out;
+        cp.rows = rows;
+        cp.splits = plan.splits;
+        if (attn::launch_combine(D, cp, st) != hipSuccess) return ATTN_ERR_HIP;
+    }
+    return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_dense(const void* q, const void* k, const void* v, void* out, int B, int N, int H,
+               int D, void* stream) {
+    if (N < 1) return ATTN_ERR_SHAPE;
+    return run(q, k, v, N, nullptr, nullptr, 0, out, B, N, H, D, 0, 0, stream);
+}
+
+int attn_prefix(const void* q, const void* kp, const void* vp, const void* kc, const void* vc,
+                void* out, int B, int Nq, int Np, int H, int D, void* stream) {
+    if (Np < 0 || Nq < 1) return ATTN_ERR_SHAPE;
+    if (!kc || !vc) return ATTN_ERR_NULL;
+    return run(q, kp, vp, Np, kc, vc, Nq, out, B, Nq, H, D, 0, 0, stream);
+}
+
+int attn_cross(const void* q, const void* k, const void* v, void* out, int B, int Nq, int Nk,
+               int H, int D, void* stream) {
+    if (Nk < 1) return ATTN_ERR_SHAPE;
+    return run(q, k, v, Nk, nullptr, nullptr, 0, out, B, Nq, H, D, 0, 0, stream);
+}
+
+int attn_fwd_ex(const void* q, const void* k0, const void* v0, int n0, const void* k1,
+                const void* v1, int n1, void* out, int B, int Nq, int H, int D, int num_splits,
+                int waves, void* stream) {
+    if ((long long)n0 + n1 < 1) return ATTN_ERR_SHAPE;
+    return run(q, k0, v0, n0, k1, v1, n1, out, B, Nq, H, D, num_splits, waves, stream);
+}
+
+int attn_plan(int B, int Nq, int Nk, int H, int D, int num_splits, int waves, int* splits,
+              int* waves_out, long long* workgroups, long long* workspace_bytes) {
+    Plan plan;
+    const int rc = make_plan(B, Nq, Nk, H, D, num_splits, waves, &plan);
+    if (rc != ATTN_OK) return rc;
+    if (splits) *splits = plan.splits;
+    if (waves_out) *waves_out = plan.waves;
+    if (workgroups) *workgroups = plan.workgroups;
+    if (workspace_bytes) *workspace_bytes = plan.workspace_bytes;
+    return ATTN_OK;
+}
+
+int attn_reserve_workspace(long long bytes) { return reserve(bytes, nullptr); }
+
+const char* attn_strerror(int code) {
+    switch (code) {
+        case ATTN_OK: return "success";
+        case ATTN_ERR_NULL: return "a required pointer is NULL";
+        case ATTN_ERR_SHAPE: return "a batch, sequence or head count is out of range";
+        case ATTN_ERR_UNSUPPORTED: return "unsupported head dimension or launch option";
+        case ATTN_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+        case ATTN_ERR_ALIAS: return "the output overlaps an input";
+        case ATTN_ERR_OVERFLOW: return "a size exceeds the kernels' index range";
+        case ATTN_ERR_WORKSPACE: return "the split-KV work space could not be allocated";
+        case ATTN_ERR_HIP: return "a HIP runtime call or kernel launch failed";
+        default: return "unknown error code";
+    }
+}
+
+int attn_abi_version(void) { return 1; }
+
+}  // extern "C"

@@ -1,0 +1,42 @@
+// Internal launch interface between the C ABI (attn_api.hip) and the kernels
+// (attn_kernels.hip). Not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+// Arguments of the fused forward kernel. Keys are segment 0 (k0/v0, n0 rows) then
+// segment 1 (k1/v1, n1 rows); all tensors [B, rows, H, D] BF16 bits.
+struct FwdParams {
+    const uint16_t* q;
+    const uint16_t* k0;
+    const uint16_t* v0;
+    const uint16_t* k1;
+    const uint16_t* v1;
+    uint16_t* out;
+    float* part_o;    // split-KV partial outputs [splits][B*Nq*H][D], FP32, normalised
+    float* part_lse;  // split-KV log2-sum-exp2 per row [splits][B*Nq*H]
+    int B, Nq, H;
+    int n0, n1;
+    int keys_per_split;  // multiple of the key tile; the last split may be shorter
+    int splits;
+    int m_blocks;  // query blocks per (batch, head)
+    float c;       // D^-0.5 * log2(e)
+};
+
+struct CombineParams {
+    const float* part_o;
+    const float* part_lse;
+    uint16_t* out;
+    long rows;  // B*Nq*H
+    int splits;
+};
+
+constexpr int kKeyTile = 64;  // keys per tile of the forward kernel
+
+hipError_t launch_fwd(int D, int waves, const FwdParams& p, long long workgroups,
+                      hipStream_t stream);
+hipError_t launch_combine(int D, const CombineParams& p, hipStream_t stream);
+
+}  // namespace attn
