@@ -1,0 +1,237 @@
+"""Benchmark of the fused attention path on one MI355X.
+
+A step is one call of the whole path on one batch of seeded synthetic input that is
+already resident in HBM: for the default workload, dense noncausal attention with
+B=1 N=4096 H=32 D=128 (BF16 in and out, FP32 accumulation), i.e. one attn_dense
+call. FLOP per step = 4*B*H*Nq*Nk*D (the QK^T and PV contractions).
+
+Output: one JSON line (rank 0) with the metric, the roofline of the dominant kernel
+(timed with HIP events on the stream the kernel is launched on) and the FP64 CPU
+oracle timed on a bounded sample of the same workload.
+
+Options beyond the common ones:
+  --workload NAME   another workload from synth.WORKLOADS (parity sizes)
+  --all             one JSON line per workload (no CPU baseline)
+  --no-cpu          skip the CPU oracle timing
+  --copy-only MiB   run only a plain device copy of that size (counter calibration)
+"""
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention TFLOP/s and % of MI355X bf16 MFMA peak, H=32 D=128 N=4096"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X published dense BF16 MFMA peak (2.5 PFLOP/s)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
+DEFAULT_WORKLOAD = "dense_b1_n4096_h32_d128"
+KERNEL_SOURCES = ["transformer_attention_dense_amd/csrc/attn_kernels.hip",
+                  "transformer_attention_dense_amd/csrc/attn_api.hip",
+                  "transformer_attention_dense_amd/csrc/attn_launch.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--all", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-only", type=int, default=0)
+    return ap.parse_args()
+
+
+def to_device(bits, torch):
+    import numpy as np
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def make_call(w, dts, attn):
+    if w.kind == "dense":
+        if w.Nk == w.Nq:
+            out = attn.dense(*dts)
+            return out, (lambda: attn.dense(*dts, out=out))
+        out = attn.cross(*dts)
+        return out, (lambda: attn.cross(*dts, out=out))
+    out = attn.prefix(*dts)
+    return out, (lambda: attn.prefix(*dts, out=out))
+
+
+def traffic_for(workload_name):
+    """HBM bytes per launch from committed counter runs, if taken on this kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = t.get("workloads", {}).get(workload_name)
+    if not entry or t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, seconds):
+    """FP64 oracle on a bounded sample of query rows of the same workload (all keys)."""
+    import numpy as np
+    import oracle
+    ts = w.tensors()
+    total_rows = w.B * w.Nq * w.H
+    flop_per_row = 4 * w.keys * w.D
+    chunk = 256
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        rows = np.arange(done, min(done + chunk, total_rows), dtype=np.int64)
+        oracle.attention_rows(ts[0], ts[1], ts[2], *ts[3:5], rows=rows)
+        done += rows.size
+        el = time.perf_counter() - t0
+        if el >= seconds or done >= total_rows:
+            break
+        chunk = min(chunk * 2, 8192)
+    rate = done * flop_per_row / el / 1e12
+    return {"value": rate, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{done} of {total_rows} query rows (first rows in [B,Nq,H] order) of "
+                      f"{w.name}, every key, FP64, {el:.1f} s"}
+
+
+def bench_one(w, steps, warmup, torch, attn):
+    ts = w.tensors()
+    dts = [to_device(t, torch) for t in ts]
+    out, call = make_call(w, dts, attn)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    # whole-job timing: exactly `steps` steps between synchronisations
+    t0 = time.perf_counter()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        call()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = ev0.elapsed_time(ev1)
+    # per-call event timing (the pages' eager method: median of event-bracketed calls)
+    samples = []
+    for _ in range(min(steps, 50)):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        call()
+        b.record(stream)
+        b.synchronize()
+        samples.append(a.elapsed_time(b) * 1000.0)
+    plan = attn.attn_plan(w.B, w.Nq, w.keys, w.H, w.D)
+    return {"wall_s": wall, "event_ms": ev_ms, "median_call_us": statistics.median(samples),
+            "plan": plan, "finite": bool(torch.isfinite(out.float()).all())}
+
+
+def record(w, r, steps, warmup, cpu):
+    ms_per_step = r["wall_s"] * 1000.0 / steps
+    value = w.flop * steps / r["wall_s"] / 1e12
+    launch_us = r["event_ms"] * 1000.0 / steps  # average duration per launch on the stream
+    achieved = w.flop / (launch_us * 1e-6) / 1e12
+    hbm = traffic_for(w.name)
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Nq": w.Nq, "Nk": w.keys, "H": w.H, "D": w.D,
+                   "kind": w.kind, "description": w.description,
+                   "splits": r["plan"]["splits"], "waves": r["plan"]["waves"],
+                   "workgroups": r["plan"]["workgroups"]},
+        "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "median_call_us": round(r["median_call_us"], 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": hbm,
+            "kernel": "attn_fwd_kernel" + ("" if r["plan"]["splits"] == 1 else
+                                           " + attn_combine_kernel"),
+            "avg_launch_us": round(launch_us, 2),
+            "algorithmic_flop_per_launch": w.flop,
+            "algorithmic_bytes_per_launch": w.algorithmic_bytes,
+            "hbm_gbs_algorithmic": round(w.algorithmic_bytes / (launch_us * 1e-6) / 1e9, 1),
+        },
+        "outputs_finite": r["finite"],
+    }
+    if w.flop / w.algorithmic_bytes < 315:  # below the ridge point: HBM bound
+        rec["roofline"].update({"bound": "hbm", "achieved": rec["roofline"]["hbm_gbs_algorithmic"],
+                                "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                "frac": round(rec["roofline"]["hbm_gbs_algorithmic"]
+                                              / PEAK_HBM_GBS, 4)})
+    if cpu is not None:
+        rec["cpu_baseline"] = cpu
+    return rec
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(sharding across GPUs is described in the design notes, not built).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import synth
+    import transformer_attention_dense_amd as attn
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    attn.library()  # fail loudly if the HIP library is missing
+
+    if args.copy_only:
+        n = args.copy_only * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(max(1, args.steps)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": max(1, args.steps)}))
+        return
+
+    names = [w.name for w in synth.WORKLOADS] if args.all else [args.workload]
+    for name in names:
+        w = synth.workload(name)
+        print(f"bench: {w.name} warmup {args.warmup} steps {args.steps}", file=sys.stderr,
+              flush=True)
+        r = bench_one(w, args.steps, args.warmup, torch, attn)
+        cpu = None
+        if not args.all and not args.no_cpu:
+            print("bench: timing the FP64 CPU oracle on a sample", file=sys.stderr, flush=True)
+            cpu = cpu_baseline(w, args.cpu_seconds)
+        print(json.dumps(record(w, r, args.steps, args.warmup, cpu)), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -81,39 +81,67 @@ __device__ __forceinline__ void decode_workgroup(int m_blocks, int bh_count, int
     split = rest / bh_count;
 }
 
+// 16-byte global -> LDS copy (global_load_lds_dwordx4). Lane i of the wave writes
+// LDS bytes [dst + 16*i, dst + 16*i + 16); dst must be the same for the whole wave.
+__device__ __forceinline__ void load16_to_lds(const uint16_t* src, char* dst) {
+    typedef __attribute__((address_space(1))) void global_void;
+    typedef __attribute__((address_space(3))) void lds_void_t;
+    __builtin_amdgcn_global_load_lds((global_void*)(const_cast<uint16_t*>(src)),
+                                     (lds_void_t*)dst, 16, 0, 0);
+}
+
+// XOR swizzle of the 16-byte chunks of LDS row r (CPR chunks per row). Chunk c of
+// row r is stored at chunk position c ^ lds_swizzle(r). The low bit of the pattern
+// comes from the row's bit log2(CPR)-1 and the upper bits from the row's low bits,
+// so (a) 16 consecutive rows read at one logical chunk hit 16 different chunk
+// positions (K operand reads) and (b) 4 consecutive rows read at a pair of chunks
+// (2m, 2m+1) hit 8 different positions (V transpose reads).
+template <int CPR>
+__device__ __forceinline__ int lds_swizzle(int r) {
+    return ((r & (CPR / 2 - 1)) << 1) | ((r / (CPR / 2)) & 1);
+}
+
 template <int D, int NW, int BN>
 __global__ __launch_bounds__(NW* kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(FwdParams p) {
     static_assert(D == 64 || D == 128, "head dim");
-    static_assert(BN % 32 == 0, "key tile");
-    constexpr int NB = BN / 32;           // 32-key blocks per tile
-    constexpr int KS = D / 16;            // MFMA k-steps over the head dim
-    constexpr int DB = D / 32;            // 32-wide head-dim blocks of O^T
-    constexpr int KSTR = D + 8;           // LDS row stride of K (elements)
-    constexpr int VSTR = D + 16;          // LDS row stride of V (elements)
-    constexpr int CPR = D / 8;            // 16-byte chunks per row
+    static_assert(BN == 64, "key tile");
+    constexpr int NB = BN / 32;            // 32-key blocks per tile
+    constexpr int KS = D / 16;             // MFMA k-steps over the head dim
+    constexpr int DB = D / 32;             // 32-wide head-dim blocks of O^T
+    constexpr int CPR = D / 8;             // 16-byte chunks per row
+    constexpr int ROWB = 2 * D;            // bytes per LDS row
+    constexpr int TILEB = BN * ROWB;       // bytes per K or V tile
     constexpr int NT = NW * kWave;
-    constexpr int PER_T = BN * CPR / NT;  // chunks per thread per tensor per tile
-    static_assert(BN * CPR % NT == 0, "loader");
+    constexpr int PER_T = BN * CPR / NT;   // 16-byte loads per thread per tensor per tile
+    static_assert(BN * CPR % NT == 0 && NT % CPR == 0, "loader");
 
-    __shared__ __attribute__((aligned(16))) uint16_t sK[BN * KSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t sV[BN * VSTR];
+    // Two stages of (K tile, V tile), rows of 2*D bytes, chunks swizzled.
+    __shared__ __attribute__((aligned(1024))) char smem[4 * TILEB];
 
     int mb, bh, split;
     decode_workgroup(p.m_blocks, p.B * p.H, mb, bh, split);
-    const int b = bh / p.H;
-    const int h = bh - b * p.H;
     const int H = p.H;
-    const int nk = p.n0 + p.n1;
+    const int b = bh / H;
+    const int h = bh - b * H;
+    const int HD = H * D;  // elements between consecutive sequence rows
+    const int n0 = p.n0;
+    const int nk = n0 + p.n1;
     const int kbeg = split * p.keys_per_split;
     const int kend = min(nk, kbeg + p.keys_per_split);
 
     const int tid = threadIdx.x;
-    const int wave = tid / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform per wave
     const int lane = tid % kWave;
     const int n = lane & 31;
     const int g = lane >> 5;
     const int q0 = mb * (NW * 32) + wave * 32;
     const bool active = q0 < p.Nq;
+
+    // Per-(batch, head) bases of the two key segments (element offsets of row 0).
+    const uint16_t* kseg0 = p.k0 + ((long)b * n0 * HD + (long)h * D);
+    const uint16_t* vseg0 = p.v0 + ((long)b * n0 * HD + (long)h * D);
+    const uint16_t* kseg1 = p.k1 ? p.k1 + ((long)b * p.n1 * HD + (long)h * D) : kseg0;
+    const uint16_t* vseg1 = p.v1 ? p.v1 + ((long)b * p.n1 * HD + (long)h * D) : vseg0;
 
     // Q^T fragments (B operand), one per 16-dim k-step: lane holds query n, dims
     // 16*ks + 8g .. +7.
@@ -126,80 +154,97 @@ __global__ __launch_bounds__(NW* kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
             qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks + 8 * g);
     }
 
+    // Loader: load round i of thread tid fills physical chunk P = i*NT + tid of a
+    // tile, i.e. row r = P / CPR at chunk position P % CPR, which holds logical chunk
+    // (P % CPR) ^ swizzle(r). Its element offset inside a tile does not depend on the
+    // tile.
+    int ld_row[PER_T];
+    int ld_off[PER_T];
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+        const int P = i * NT + tid;
+        const int r = P / CPR;
+        const int c = (P % CPR) ^ lds_swizzle<CPR>(r);
+        ld_row[i] = r;
+        ld_off[i] = r * HD + c * 8;
+    }
+
+    // LDS: K slots 0 and 1, then V slots 0 and 1.
+    auto issue = [&](const uint16_t* seg0, const uint16_t* seg1, int t0, char* slot) {
+        char* const dst = slot + wave * kWave * 16;
+        const bool whole = (t0 + BN <= kend) && (t0 + BN <= n0 || t0 >= n0);
+        if (whole) {
+            const uint16_t* base = (t0 < n0) ? seg0 + (long)t0 * HD : seg1 + (long)(t0 - n0) * HD;
+#pragma unroll
+            for (int i = 0; i < PER_T; ++i) load16_to_lds(base + ld_off[i], dst + i * NT * 16);
+        } else {
+            // ragged or segment-straddling tile: clamp rows into [t0, kend) and pick
+            // the segment per row
+#pragma unroll
+            for (int i = 0; i < PER_T; ++i) {
+                const int key = min(t0 + ld_row[i], kend - 1);
+                const int co = ld_off[i] - ld_row[i] * HD;
+                const uint16_t* src =
+                    key < n0 ? seg0 + (long)key * HD : seg1 + (long)(key - n0) * HD;
+                load16_to_lds(src + co, dst + i * NT * 16);
+            }
+        }
+    };
+    auto issue_k = [&](int t0, int slot) { issue(kseg0, kseg1, t0, smem + slot * TILEB); };
+    auto issue_v = [&](int t0, int slot) { issue(vseg0, vseg1, t0, smem + (2 + slot) * TILEB); };
+
+    // Per-lane LDS byte offsets of the K operand reads (per k-step) and of the V
+    // transpose reads (per head-dim block and 8-key half), relative to a K or V slot;
+    // key blocks and 16-key steps add whole rows.
+    int koff[KS];
+    {
+        const int t = lds_swizzle<CPR>(n) ^ g;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) koff[ks] = n * ROWB + 16 * ((2 * ks) ^ t);
+    }
+    constexpr int VH = (D == 128) ? 2 : 1;  // distinct swizzles over the 8-key halves
+    int voff[DB][VH];
+    {
+        const int tr_r = (lane & 15) >> 2;
+        const int tr_q = lane & 3;
+        const int half = (lane >> 4) & 1;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int h2 = 0; h2 < VH; ++h2) {
+                const int row = 8 * h2 + 4 * g + tr_r;
+                const int c = (4 * db + 2 * half + (tr_q >> 1)) ^ lds_swizzle<CPR>(row);
+                voff[db][h2] = row * ROWB + 16 * c + 8 * (tr_q & 1);
+            }
+    }
+
     f32x16 o[DB];
 #pragma unroll
     for (int i = 0; i < DB; ++i) o[i] = f32x16{};
     float m_ref = -INFINITY;  // running reference maximum (raw score units)
-    float l_part = 0.f;       // this lane's partial row sum
+    float l_part = 0.f;       // this lane's partial row sum (of BF16-rounded probabilities)
     const float c = p.c;
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-    // Global -> register staging of one K/V tile.
-    u32x4 kreg[PER_T], vreg[PER_T];
-    auto load_tile = [&](int t0) {
-#pragma unroll
-        for (int i = 0; i < PER_T; ++i) {
-            const int ch = tid + i * NT;
-            const int row = ch / CPR;
-            const int col = (ch % CPR) * 8;
-            const int key = min(t0 + row, kend - 1);
-            const uint16_t* ks;
-            const uint16_t* vs;
-            if (key < p.n0) {
-                const long off = ((long)(b * p.n0 + key) * H + h) * D + col;
-                ks = p.k0 + off;
-                vs = p.v0 + off;
-            } else {
-                const long off = ((long)(b * p.n1 + (key - p.n0)) * H + h) * D + col;
-                ks = p.k1 + off;
-                vs = p.v1 + off;
-            }
-            kreg[i] = *reinterpret_cast<const u32x4*>(ks);
-            vreg[i] = *reinterpret_cast<const u32x4*>(vs);
-        }
-    };
-    auto store_tile = [&]() {
-#pragma unroll
-        for (int i = 0; i < PER_T; ++i) {
-            const int ch = tid + i * NT;
-            const int row = ch / CPR;
-            const int col = (ch % CPR) * 8;
-            *reinterpret_cast<u32x4*>(&sK[row * KSTR + col]) = kreg[i];
-            *reinterpret_cast<u32x4*>(&sV[row * VSTR + col]) = vreg[i];
-        }
-    };
-
-    // Per-lane LDS offsets (elements).
-    const int k_off = n * KSTR + 8 * g;  // + (kb*32)*KSTR + 16*ks
-    const int tr_r = (lane & 15) >> 2;
-    const int tr_q = lane & 3;
-    const int v_off = (4 * g + tr_r) * VSTR + 16 * ((lane >> 4) & 1) + 4 * tr_q;
-
-    const int ntiles = (kend - kbeg + BN - 1) / BN;
-    load_tile(kbeg);
-    for (int t = 0; t < ntiles; ++t) {
-        const int t0 = kbeg + t * BN;
-        __syncthreads();
-        store_tile();
-        __syncthreads();
-        if (t + 1 < ntiles) load_tile(t0 + BN);
-        if (!active) continue;
-
-        // ---- S^T = K Q^T for the tile
-        f32x16 s[NB];
+    // S^T = K Q^T for one K tile.
+    auto qk = [&](const char* kt, f32x16 (&s)[NB]) {
 #pragma unroll
         for (int kb = 0; kb < NB; ++kb) s[kb] = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
             for (int kb = 0; kb < NB; ++kb) {
-                const bf16x8 a =
-                    *reinterpret_cast<const bf16x8*>(&sK[k_off + kb * 32 * KSTR + 16 * ks]);
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + koff[ks] + kb * 32 * ROWB);
                 s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
             }
         }
+    };
 
-        // ---- mask keys past the end of this range (ragged last tile)
-        if (t0 + BN > kend) {
+    // Online softmax of one tile of scores starting at key t0 (exp2 domain); returns
+    // the BF16 probabilities as B operands of the PV product.
+    auto softmax = [&](f32x16 (&s)[NB], int t0, bf16x8 (&pf)[NB][2]) {
+        if (t0 + BN > kend) {  // keys past the end of this range (ragged last tile)
 #pragma unroll
             for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
@@ -208,8 +253,6 @@ __global__ __launch_bounds__(NW* kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
                     if (key >= kend) s[kb][r] = -INFINITY;
                 }
         }
-
-        // ---- online softmax (exp2 domain)
         float mx = s[0][0];
 #pragma unroll
         for (int kb = 0; kb < NB; ++kb)
@@ -226,34 +269,66 @@ __global__ __launch_bounds__(NW* kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
             m_ref = m_new;
         }
         const float mc = (m_ref == -INFINITY) ? 0.f : m_ref * c;
-        bf16x8 pf[NB][2];
 #pragma unroll
         for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -mc));
-                l_part += e;
-                pf[kb][r >> 3][r & 7] = (__bf16)e;
+            for (int r = 0; r < 16; r += 2) {
+                const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -mc));
+                const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r + 1], c, -mc));
+                const bf16x2 pk = {(__bf16)e0, (__bf16)e1};
+                l_part = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, l_part, false);
+                pf[kb][r >> 3][r & 7] = pk[0];
+                pf[kb][r >> 3][(r & 7) + 1] = pk[1];
             }
+    };
 
-        // ---- O^T += V^T P^T
+    // O^T += V^T P^T for one V tile.
+    auto pv = [&](const char* vt, const bf16x8 (&pf)[NB][2]) {
 #pragma unroll
         for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
-                const int rowbase = kb * 32 + 16 * tt;
+                const int rowbase = (kb * 32 + 16 * tt) * ROWB;
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
-                    const int off = v_off + rowbase * VSTR + 32 * db;
-                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_i16x4*)((lds_u16*)sV + off));
-                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_i16x4*)((lds_u16*)sV + off + 8 * VSTR));
+                    const int o_lo = voff[db][0] + rowbase;
+                    const int o_hi =
+                        (VH == 2 ? voff[db][VH - 1] : voff[db][0] + 8 * ROWB) + rowbase;
+                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + o_lo));
+                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + o_hi));
                     const i16x8 a16 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                    const bf16x8 a = __builtin_bit_cast(bf16x8, a16);
-                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kb][tt], o[db], 0, 0, 0);
+                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a16),
+                                                                    pf[kb][tt], o[db], 0, 0, 0);
                 }
             }
+    };
+
+    // Pipeline: while the softmax of tile t runs on the VALU, the MFMAs of S(t+1)
+    // proceed; K(t+2) and V(t+1) stream into the free slots during iteration t.
+    const int ntiles = (kend - kbeg + BN - 1) / BN;
+    issue_k(kbeg, 0);
+    issue_v(kbeg, 0);
+    if (ntiles > 1) issue_k(kbeg + BN, 1);
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    f32x16 s_cur[NB];
+    if (active) qk(smem, s_cur);
+    __syncthreads();  // K slot 0 is refilled in the first iteration
+    for (int t = 0; t < ntiles; ++t) {
+        const int t0 = kbeg + t * BN;
+        if (t + 2 < ntiles) issue_k(t0 + 2 * BN, t & 1);
+        if (t + 1 < ntiles) issue_v(t0 + BN, (t + 1) & 1);
+        if (active) {
+            f32x16 s_next[NB];
+            if (t + 1 < ntiles) qk(smem + ((t + 1) & 1) * TILEB, s_next);
+            bf16x8 pf[NB][2];
+            softmax(s_cur, t0, pf);
+            pv(smem + (2 + (t & 1)) * TILEB, pf);
+#pragma unroll
+            for (int kb = 0; kb < NB; ++kb) s_cur[kb] = s_next[kb];
+        }
+        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
     }
 
     if (!active) return;
