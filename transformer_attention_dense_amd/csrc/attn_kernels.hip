@@ -33,6 +33,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 #include "attn_launch.h"
 
 namespace attn {
@@ -42,6 +45,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -81,6 +85,16 @@ __device__ __forceinline__ void decode_workgroup(int m_blocks, int bh_count, int
     split = rest / bh_count;
 }
 
+// Calls f(std::integral_constant<int, i>{}) for i = 0 .. N-1 (compile-time indices).
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+    (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 // 16-byte global -> LDS copy (global_load_lds_dwordx4). Lane i of the wave writes
 // LDS bytes [dst + 16*i, dst + 16*i + 16); dst must be the same for the whole wave.
 __device__ __forceinline__ void load16_to_lds(const uint16_t* src, char* dst) {
@@ -90,21 +104,42 @@ __device__ __forceinline__ void load16_to_lds(const uint16_t* src, char* dst) {
                                      (lds_void_t*)dst, 16, 0, 0);
 }
 
-// XOR swizzle of the 16-byte chunks of LDS row r (CPR chunks per row). Chunk c of
-// row r is stored at chunk position c ^ lds_swizzle(r). The low bit of the pattern
-// comes from the row's bit log2(CPR)-1 and the upper bits from the row's low bits,
-// so (a) 16 consecutive rows read at one logical chunk hit 16 different chunk
-// positions (K operand reads) and (b) 4 consecutive rows read at a pair of chunks
-// (2m, 2m+1) hit 8 different positions (V transpose reads).
+// XOR swizzle of the 16-byte chunks of LDS row r (CPR chunks per row, period 16
+// rows). Chunk c of row r is stored at chunk position c ^ lds_swizzle(r). Chosen so
+// that (a) the 16 lanes of a K operand read (16 consecutive rows, one logical chunk)
+// hit 64 different banks, and (b) the 32 lanes of a V transpose read (4 consecutive
+// rows, 4 consecutive chunks) hit 64 different banks: the pattern keeps aligned
+// groups of 4 chunks together and moves whole groups between those rows.
+//   D = 128 (16 chunks, one row = all 64 banks): ((r & 3) << 2) | ((r >> 2) & 3)
+//   D = 64 (8 chunks, rows of one parity share a bank half): x = (r >> 1) & 7,
+//   ((x & 1) << 2) | ((x >> 1) & 3)
 template <int CPR>
 __device__ __forceinline__ int lds_swizzle(int r) {
-    return ((r & (CPR / 2 - 1)) << 1) | ((r / (CPR / 2)) & 1);
+    if constexpr (CPR == 16) {
+        return ((r & 3) << 2) | ((r >> 2) & 3);
+    } else {
+        const int x = (r >> 1) & 7;
+        return ((x & 1) << 2) | ((x >> 1) & 3);
+    }
+}
+
+// Workgroup barrier that first waits until at most N of this wave's global->LDS
+// copies are outstanding and all of its LDS reads have returned. Unlike
+// __syncthreads(), later copies may stay in flight across the barrier. The empty asm
+// statements keep the compiler from moving memory accesses across it.
+template <int N>
+__device__ __forceinline__ void barrier_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
 }
 
 template <int D, int NW, int BN>
 __global__ __launch_bounds__(NW* kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(FwdParams p) {
     static_assert(D == 64 || D == 128, "head dim");
-    static_assert(BN == 64, "key tile");
+    static_assert(BN == 32 || BN == 64, "key tile");
     constexpr int NB = BN / 32;            // 32-key blocks per tile
     constexpr int KS = D / 16;             // MFMA k-steps over the head dim
     constexpr int DB = D / 32;             // 32-wide head-dim blocks of O^T
@@ -115,8 +150,9 @@ __global__ __launch_bounds__(NW* kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
     constexpr int PER_T = BN * CPR / NT;   // 16-byte loads per thread per tensor per tile
     static_assert(BN * CPR % NT == 0 && NT % CPR == 0, "loader");
 
-    // Two stages of (K tile, V tile), rows of 2*D bytes, chunks swizzled.
-    __shared__ __attribute__((aligned(1024))) char smem[4 * TILEB];
+    // Three K slots then three V slots, rows of 2*D bytes, chunks swizzled.
+    constexpr int NSLOT = 3;
+    __shared__ __attribute__((aligned(1024))) char smem[2 * NSLOT * TILEB];
 
     int mb, bh, split;
     decode_workgroup(p.m_blocks, p.B * p.H, mb, bh, split);
@@ -156,34 +192,39 @@ __global__ __launch_bounds__(NW* kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
 
     // Loader: load round i of thread tid fills physical chunk P = i*NT + tid of a
     // tile, i.e. row r = P / CPR at chunk position P % CPR, which holds logical chunk
-    // (P % CPR) ^ swizzle(r). Its element offset inside a tile does not depend on the
-    // tile.
-    int ld_row[PER_T];
-    int ld_off[PER_T];
+    // (P % CPR) ^ swizzle(r). Rounds advance by RSTEP rows; the swizzle pattern has a
+    // period of SWP rows, so the per-lane offsets repeat every SWP / RSTEP rounds.
+    constexpr int RSTEP = NT / CPR;
+    constexpr int SWP = 16;
+    constexpr int NPAT = (RSTEP % SWP == 0) ? 1 : SWP / RSTEP;
+    static_assert(RSTEP % SWP == 0 || SWP % RSTEP == 0, "loader pattern");
+    int ld_off[NPAT];
 #pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
+    for (int i = 0; i < NPAT; ++i) {
         const int P = i * NT + tid;
         const int r = P / CPR;
         const int c = (P % CPR) ^ lds_swizzle<CPR>(r);
-        ld_row[i] = r;
         ld_off[i] = r * HD + c * 8;
     }
 
-    // LDS: K slots 0 and 1, then V slots 0 and 1.
     auto issue = [&](const uint16_t* seg0, const uint16_t* seg1, int t0, char* slot) {
         char* const dst = slot + wave * kWave * 16;
         const bool whole = (t0 + BN <= kend) && (t0 + BN <= n0 || t0 >= n0);
         if (whole) {
-            const uint16_t* base = (t0 < n0) ? seg0 + (long)t0 * HD : seg1 + (long)(t0 - n0) * HD;
+            const long rowoff = (t0 < n0) ? (long)t0 * HD : (long)(t0 - n0) * HD;
+            const uint16_t* base = ((t0 < n0) ? seg0 : seg1) + rowoff;
 #pragma unroll
-            for (int i = 0; i < PER_T; ++i) load16_to_lds(base + ld_off[i], dst + i * NT * 16);
+            for (int i = 0; i < PER_T; ++i)
+                load16_to_lds(base + (long)(i / NPAT) * NPAT * RSTEP * HD + ld_off[i % NPAT],
+                              dst + i * NT * 16);
         } else {
             // ragged or segment-straddling tile: clamp rows into [t0, kend) and pick
             // the segment per row
 #pragma unroll
             for (int i = 0; i < PER_T; ++i) {
-                const int key = min(t0 + ld_row[i], kend - 1);
-                const int co = ld_off[i] - ld_row[i] * HD;
+                const int r = (i * NT + tid) / CPR;
+                const int key = min(t0 + r, kend - 1);
+                const int co = ld_off[i % NPAT] - (r - (i / NPAT) * NPAT * RSTEP) * HD;
                 const uint16_t* src =
                     key < n0 ? seg0 + (long)key * HD : seg1 + (long)(key - n0) * HD;
                 load16_to_lds(src + co, dst + i * NT * 16);
@@ -191,7 +232,9 @@ __global__ __launch_bounds__(NW* kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
         }
     };
     auto issue_k = [&](int t0, int slot) { issue(kseg0, kseg1, t0, smem + slot * TILEB); };
-    auto issue_v = [&](int t0, int slot) { issue(vseg0, vseg1, t0, smem + (2 + slot) * TILEB); };
+    auto issue_v = [&](int t0, int slot) {
+        issue(vseg0, vseg1, t0, smem + (NSLOT + slot) * TILEB);
+    };
 
     // Per-lane LDS byte offsets of the K operand reads (per k-step) and of the V
     // transpose reads (per head-dim block and 8-key half), relative to a K or V slot;
@@ -202,7 +245,7 @@ __global__ __launch_bounds__(NW* kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) koff[ks] = n * ROWB + 16 * ((2 * ks) ^ t);
     }
-    constexpr int VH = (D == 128) ? 2 : 1;  // distinct swizzles over the 8-key halves
+    constexpr int VH = 2;  // the two 8-key halves of a 16-key step use different swizzles
     int voff[DB][VH];
     {
         const int tr_r = (lane & 15) >> 2;
@@ -224,41 +267,58 @@ __global__ __launch_bounds__(NW* kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
     float m_ref = -INFINITY;  // running reference maximum (raw score units)
     float l_part = 0.f;       // this lane's partial row sum (of BF16-rounded probabilities)
     const float c = p.c;
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-    // S^T = K Q^T for one K tile.
-    auto qk = [&](const char* kt, f32x16 (&s)[NB]) {
-#pragma unroll
-        for (int kb = 0; kb < NB; ++kb) s[kb] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-            for (int kb = 0; kb < NB; ++kb) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + koff[ks] + kb * 32 * ROWB);
-                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
-            }
-        }
-    };
+    constexpr int NQ = KS * NB;         // QK^T MFMAs per tile
+    constexpr int NP = 2 * NB * DB;     // PV MFMAs per tile
+    constexpr int NF = NQ + NP;         // LDS operand fragments per pipelined tile
+    constexpr int NPAIR = NB * 8;       // exp pairs per lane per tile
+    // exp pairs per step of the second block, so that every 16-key chunk of P is
+    // complete before its first PV MFMA
+    constexpr int QUOTA = (NPAIR + (NQ / 2 + NP - DB) - 1) / (NQ / 2 + NP - DB);
 
-    // Online softmax of one tile of scores starting at key t0 (exp2 domain); returns
-    // the BF16 probabilities as B operands of the PV product.
-    auto softmax = [&](f32x16 (&s)[NB], int t0, bf16x8 (&pf)[NB][2]) {
-        if (t0 + BN > kend) {  // keys past the end of this range (ragged last tile)
-#pragma unroll
-            for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = t0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-                    if (key >= kend) s[kb][r] = -INFINITY;
-                }
-        }
-        float mx = s[0][0];
+    // K operand fragment m of a K tile (k-step m / NB, key block m % NB).
+    auto read_k = [&](const char* kt, auto mc) {
+        constexpr int m = decltype(mc)::value;
+        return *reinterpret_cast<const bf16x8*>(kt + koff[m / NB] + (m % NB) * 32 * ROWB);
+    };
+    // V^T operand fragment j of a V tile: 16-key chunk j / DB = (kb, tt), head-dim
+    // block j % DB; two transpose reads of 4 keys each.
+    auto read_v = [&](const char* vt, auto jc) {
+        constexpr int j = decltype(jc)::value;
+        constexpr int cc = j / DB, kb = cc / 2, tt = cc % 2, db = j % DB;
+        constexpr int rowbase = (kb * 32 + 16 * tt) * ROWB;
+        const int o_lo = voff[db][0] + rowbase;
+        const int o_hi = (VH == 2 ? voff[db][VH - 1] : voff[db][0] + 8 * ROWB) + rowbase;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + o_lo));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + o_hi));
+        const i16x8 a16 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        return __builtin_bit_cast(bf16x8, a16);
+    };
+    // P for one pair of keys: exp2(s*c - m*c) rounded to BF16; the row sum adds the
+    // rounded values.
+    auto exp_pair = [&](const f32x16 (&s)[NB], auto pc, float mc, bf16x8 (&pf)[NB][2]) {
+        constexpr int pi = decltype(pc)::value;
+        constexpr int cc = pi / 4, kb = cc / 2, tt = cc % 2, r = 8 * tt + 2 * (pi % 4);
+        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -mc));
+        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r + 1], c, -mc));
+        const bf16x2 pk = {(__bf16)e0, (__bf16)e1};
+        l_part = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, l_part, false);
+        pf[kb][tt][r & 7] = pk[0];
+        pf[kb][tt][(r & 7) + 1] = pk[1];
+    };
+    auto mask_tail = [&](f32x16 (&s)[NB], int t0) {
 #pragma unroll
         for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-        mx = wave_swap_max(mx);
+            for (int r = 0; r < 16; ++r) {
+                const int key = t0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+                if (key >= kend) s[kb][r] = -INFINITY;
+            }
+    };
+    // Raises the reference maximum (and rescales O and l) only when some row's
+    // tile maximum exceeds it by more than 2^kRescaleLog2 in the exp2 domain.
+    auto update_max = [&](float mx) {
         const bool need = (mx - m_ref) * c > kRescaleLog2;
         if (__builtin_amdgcn_ballot_w64(need) != 0) {
             const float m_new = fmaxf(m_ref, mx);
@@ -268,67 +328,136 @@ __global__ __launch_bounds__(NW* kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
             for (int i = 0; i < DB; ++i) o[i] *= alpha;
             m_ref = m_new;
         }
-        const float mc = (m_ref == -INFINITY) ? 0.f : m_ref * c;
-#pragma unroll
-        for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -mc));
-                const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r + 1], c, -mc));
-                const bf16x2 pk = {(__bf16)e0, (__bf16)e1};
-                l_part = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, l_part, false);
-                pf[kb][r >> 3][r & 7] = pk[0];
-                pf[kb][r >> 3][(r & 7) + 1] = pk[1];
-            }
+        return (m_ref == -INFINITY) ? 0.f : m_ref * c;
+    };
+    auto sv = [&](const f32x16 (&s)[NB], int e) -> float { return s[e / 16][e % 16]; };
+
+    // S^T = K Q^T for one K tile, unpipelined (first tile).
+    auto qk_full = [&](const char* kt, f32x16 (&s)[NB]) {
+        static_for<NQ>([&](auto mc) {
+            constexpr int m = decltype(mc)::value;
+            const bf16x8 a = read_k(kt, mc);
+            s[m % NB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                a, qf[m / NB], m < NB ? f32x16{} : s[m % NB], 0, 0, 0);
+        });
     };
 
-    // O^T += V^T P^T for one V tile.
-    auto pv = [&](const char* vt, const bf16x8 (&pf)[NB][2]) {
-#pragma unroll
-        for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                const int rowbase = (kb * 32 + 16 * tt) * ROWB;
-#pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    const int o_lo = voff[db][0] + rowbase;
-                    const int o_hi =
-                        (VH == 2 ? voff[db][VH - 1] : voff[db][0] + 8 * ROWB) + rowbase;
-                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + o_lo));
-                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + o_hi));
-                    const i16x8 a16 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a16),
-                                                                    pf[kb][tt], o[db], 0, 0, 0);
-                }
+    // One pipelined tile: the MFMAs of S(t+1) = K(t+1) Q^T run while S(t) is reduced
+    // and exponentiated; then O += P(t) V(t). LDS fragments are read two MFMAs ahead
+    // and each MFMA is paired with a fixed slice of VALU work between scheduling
+    // fences.
+    auto tile_pipelined = [&](const f32x16 (&sc)[NB], f32x16 (&sn)[NB], const char* kt,
+                              const char* vt) {
+        bf16x8 fr[3];
+        auto read_f = [&](auto fc) {
+            constexpr int f = decltype(fc)::value;
+            if constexpr (f < NQ)
+                fr[f % 3] = read_k(kt, fc);
+            else
+                fr[f % 3] = read_v(vt, std::integral_constant<int, f - NQ>{});
+        };
+        read_f(std::integral_constant<int, 0>{});
+        read_f(std::integral_constant<int, 1>{});
+        float mx = fmaxf(sv(sc, 0), sv(sc, 1));
+        // score pairs folded into the maximum per step of block 1
+        constexpr int MPS = (NB * 8 - 1 + NQ / 2 - 1) / (NQ / 2);
+        __builtin_amdgcn_sched_barrier(0);
+        // block 1: S(t+1) for the first half of the k-steps; row maximum of S(t)
+        static_for<NQ / 2>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            read_f(std::integral_constant<int, i + 2>{});
+            sn[i % NB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                fr[i % 3], qf[i / NB], i < NB ? f32x16{} : sn[i % NB], 0, 0, 0);
+            static_for<MPS>([&](auto qc) {
+                constexpr int e = 2 + 2 * (i * MPS + decltype(qc)::value);
+                if constexpr (e + 1 < NB * 16) mx = fmaxf(fmaxf(mx, sv(sc, e)), sv(sc, e + 1));
+            });
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        const float mc = update_max(wave_swap_max(mx));
+        // block 2: rest of S(t+1); exponentials of S(t); O += P(t) V(t)
+        bf16x8 pf[NB][2];
+        static_for<NQ / 2 + NP>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            constexpr int f = NQ / 2 + i;
+            if constexpr (f + 2 < NF) read_f(std::integral_constant<int, f + 2>{});
+            if constexpr (f < NQ) {
+                sn[f % NB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[f % 3], qf[f / NB],
+                                                                     sn[f % NB], 0, 0, 0);
+            } else {
+                constexpr int j = f - NQ;
+                constexpr int cc = j / DB, kb = cc / 2, tt = cc % 2, db = j % DB;
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[f % 3], pf[kb][tt], o[db], 0,
+                                                                0, 0);
             }
+            static_for<QUOTA>([&](auto qc) {
+                constexpr int pi = i * QUOTA + decltype(qc)::value;
+                if constexpr (pi < NPAIR) exp_pair(sc, std::integral_constant<int, pi>{}, mc, pf);
+            });
+            __builtin_amdgcn_sched_barrier(0);
+        });
     };
 
-    // Pipeline: while the softmax of tile t runs on the VALU, the MFMAs of S(t+1)
-    // proceed; K(t+2) and V(t+1) stream into the free slots during iteration t.
+    // Last tile of the range: no next tile; keys past the end are masked.
+    auto tile_last = [&](f32x16 (&sc)[NB], int t0, const char* vt) {
+        if (t0 + BN > kend) mask_tail(sc, t0);
+        float mx = sv(sc, 0);
+#pragma unroll
+        for (int e = 1; e < NB * 16; ++e) mx = fmaxf(mx, sv(sc, e));
+        const float mc = update_max(wave_swap_max(mx));
+        bf16x8 pf[NB][2];
+        static_for<NPAIR>([&](auto pc) { exp_pair(sc, pc, mc, pf); });
+        static_for<NP>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            constexpr int cc = j / DB, kb = cc / 2, tt = cc % 2, db = j % DB;
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_v(vt, jc), pf[kb][tt], o[db], 0,
+                                                            0, 0);
+        });
+    };
+
+    // Pipeline over the tiles of the range. Tile j of K and of V lives in slot j % 3.
+    // During tile t the loads of K(t+3) and V(t+2) are issued; at its end only the
+    // loads issued during tile t may still be in flight (K(t+2) and V(t+1) must have
+    // landed). One barrier per tile.
     const int ntiles = (kend - kbeg + BN - 1) / BN;
+    auto kslot = [&](int j) { return smem + (j % NSLOT) * TILEB; };
+    auto vslot = [&](int j) { return smem + (NSLOT + j % NSLOT) * TILEB; };
     issue_k(kbeg, 0);
     issue_v(kbeg, 0);
-    if (ntiles > 1) issue_k(kbeg + BN, 1);
-    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    f32x16 s_cur[NB];
-    if (active) qk(smem, s_cur);
-    __syncthreads();  // K slot 0 is refilled in the first iteration
-    for (int t = 0; t < ntiles; ++t) {
+    if (ntiles > 1) {
+        issue_k(kbeg + BN, 1);
+        issue_v(kbeg + BN, 1);
+    }
+    if (ntiles > 2) issue_k(kbeg + 2 * BN, 2);
+    barrier_vmcnt<0>();
+    f32x16 sA[NB], sB[NB];
+    if (active) qk_full(smem, sA);
+    barrier_vmcnt<2 * PER_T>();  // K slot 0 is refilled during the first tile
+
+    auto step = [&](int t, const f32x16 (&sc)[NB], f32x16 (&sn)[NB]) {
         const int t0 = kbeg + t * BN;
-        if (t + 2 < ntiles) issue_k(t0 + 2 * BN, t & 1);
-        if (t + 1 < ntiles) issue_v(t0 + BN, (t + 1) & 1);
-        if (active) {
-            f32x16 s_next[NB];
-            if (t + 1 < ntiles) qk(smem + ((t + 1) & 1) * TILEB, s_next);
-            bf16x8 pf[NB][2];
-            softmax(s_cur, t0, pf);
-            pv(smem + (2 + (t & 1)) * TILEB, pf);
-#pragma unroll
-            for (int kb = 0; kb < NB; ++kb) s_cur[kb] = s_next[kb];
-        }
-        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
+        const bool more_k = t + 3 < ntiles;
+        const bool more_v = t + 2 < ntiles;
+        if (more_k) issue_k(t0 + 3 * BN, t % NSLOT);
+        if (more_v) issue_v(t0 + 2 * BN, (t + 2) % NSLOT);
+        if (active) tile_pipelined(sc, sn, kslot(t + 1), vslot(t));
+        if (more_k)
+            barrier_vmcnt<2 * PER_T>();
+        else if (more_v)
+            barrier_vmcnt<PER_T>();
+        else
+            barrier_vmcnt<0>();
+    };
+    int t = 0;
+    for (; t + 2 < ntiles; t += 2) {
+        step(t, sA, sB);
+        step(t + 1, sB, sA);
+    }
+    if (t + 1 < ntiles) {
+        step(t, sA, sB);
+        if (active) tile_last(sB, kbeg + (t + 1) * BN, vslot(t + 1));
+    } else if (active) {
+        tile_last(sA, kbeg + t * BN, vslot(t));
     }
 
     if (!active) return;
@@ -409,8 +538,8 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(CombineParams p) {
 
 template <int D, int NW>
 static hipError_t launch_fwd_t(const FwdParams& p, long long workgroups, hipStream_t stream) {
-    hipLaunchKernelGGL((attn_fwd_kernel<D, NW, 64>), dim3((unsigned)workgroups), dim3(NW * kWave),
-                       0, stream, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, NW, key_tile(D)>), dim3((unsigned)workgroups),
+                       dim3(NW * kWave), 0, stream, p);
     return hipGetLastError();
 }
 

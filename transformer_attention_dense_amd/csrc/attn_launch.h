@@ -33,7 +33,10 @@ struct CombineParams {
     int splits;
 };
 
-constexpr int kKeyTile = 64;  // keys per tile of the forward kernel
+// Keys per tile of the forward kernel: 32 at D = 128 (keeps two waves per SIMD within
+// the register budget), 64 at D = 64. Split ranges are multiples of 64 keys.
+constexpr int key_tile(int D) { return D == 128 ? 32 : 64; }
+constexpr int kKeyTile = 64;
 
 hipError_t launch_fwd(int D, int waves, const FwdParams& p, long long workgroups,
                       hipStream_t stream);
