@@ -31,6 +31,8 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X published dense BF16 MFMA peak (2.5 PFLOP/s
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
 DEFAULT_WORKLOAD = "dense_b1_n4096_h32_d128"
 KERNEL_SOURCES = ["transformer_attention_dense_amd/csrc/attn_kernels.hip",
+                  "transformer_attention_dense_amd/csrc/attn_pingpong.hip",
+                  "transformer_attention_dense_amd/csrc/attn_device.h",
                   "transformer_attention_dense_amd/csrc/attn_api.hip",
                   "transformer_attention_dense_amd/csrc/attn_launch.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")

@@ -84,8 +84,9 @@ int attn_cross(const void* q, const void* k, const void* v, void* out, int B, in
  * n0 + n1 >= 1, and a segment with zero rows may have NULL pointers.
  * num_splits: 0 = automatic, otherwise the number of key ranges computed in parallel
  *             and merged by a combine step (clamped to the number of key tiles).
- * waves:      0 = automatic, otherwise 2 or 4 wavefronts (32 query rows each) per
- *             workgroup.
+ * waves:      0 = automatic, otherwise 2, 4 or 8 wavefronts (32 query rows each)
+ *             per workgroup; 8 selects the ping-pong schedule (two wave groups
+ *             alternating matrix and softmax phases).
  * Results for any options agree with each other up to floating-point rounding.
  */
 int attn_fwd_ex(const void* q, const void* k0, const void* v0, int n0, const void* k1,

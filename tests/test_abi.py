@@ -73,8 +73,9 @@ def test_unsupported_head_dim_rejected(D):
 def test_bad_launch_options_rejected():
     assert attn.attn_fwd_ex(A, A + MB, A + 2 * MB, 4, None, None, 0, A + 3 * MB, 1, 4, 1, 64,
                             -1, 0, None) == -3
-    assert attn.attn_fwd_ex(A, A + MB, A + 2 * MB, 4, None, None, 0, A + 3 * MB, 1, 4, 1, 64,
-                            0, 3, None) == -3
+    for w in (1, 3, 6, 16):
+        assert attn.attn_fwd_ex(A, A + MB, A + 2 * MB, 4, None, None, 0, A + 3 * MB, 1, 4, 1,
+                                64, 0, w, None) == -3
 
 
 def test_misaligned_pointers_rejected():
@@ -99,11 +100,18 @@ def test_sizes_beyond_index_range_rejected():
 
 
 def test_plan_for_the_workloads():
+    # enough query blocks to fill 256 CUs with 8-wave (256-row) workgroups
     p1 = attn.attn_plan(1, 4096, 4096, 32, 128)
-    assert p1["splits"] == 1 and p1["waves"] == 4 and p1["workgroups"] == 32 * 32
+    assert p1["splits"] == 1 and p1["waves"] == 8 and p1["workgroups"] == 16 * 32
     assert p1["workspace_bytes"] == 0
     p3 = attn.attn_plan(1, 4096, 5120, 32, 128)
-    assert p3["splits"] == 1 and p3["workgroups"] == 1024
+    assert p3["splits"] == 1 and p3["waves"] == 8 and p3["workgroups"] == 512
+    p2 = attn.attn_plan(2, 16384, 16384, 32, 64)
+    assert p2["waves"] == 8 and p2["workgroups"] == 64 * 64
+    # too few 256-row blocks: 4-wave workgroups; short sequences: 2 waves
+    p0 = attn.attn_plan(1, 256, 256, 32, 64)
+    assert p0["waves"] == 4
+    assert attn.attn_plan(1024, 64, 64, 32, 64)["waves"] == 2
     # few query blocks and long keys -> the keys are split and a work space is needed
     ps = attn.attn_plan(1, 64, 8192, 2, 128)
     assert ps["splits"] > 1 and ps["workspace_bytes"] > 0

@@ -51,7 +51,7 @@ DENSE_CASES = [
 
 
 @pytest.mark.parametrize("B,Nq,Nk,H,D", DENSE_CASES)
-@pytest.mark.parametrize("splits,waves", [(0, 0), (1, 4), (1, 2), (3, 4), (7, 2)])
+@pytest.mark.parametrize("splits,waves", [(0, 0), (1, 4), (1, 2), (3, 4), (7, 2), (1, 8), (3, 8)])
 def test_dense_small_all_elements(B, Nq, Nk, H, D, splits, waves):
     say(f"dense B{B} Nq{Nq} Nk{Nk} H{H} D{D} splits{splits} waves{waves}")
     w = synth.small("dense", B, Nq, H, D, 300 + Nq + 3 * Nk, Nk=Nk, sigma_qk=2.0)
@@ -62,14 +62,14 @@ def test_dense_small_all_elements(B, Nq, Nk, H, D, splits, waves):
 
 
 @pytest.mark.parametrize("Np", [0, 1, 17, 64, 100])
-@pytest.mark.parametrize("splits", [0, 1, 4])
-def test_prefix_small_all_elements(Np, splits):
+@pytest.mark.parametrize("splits,waves", [(0, 0), (1, 0), (4, 0), (1, 8), (2, 8)])
+def test_prefix_small_all_elements(Np, splits, waves):
     B, Nq, H, D = 2, 77, 3, 128
-    say(f"prefix Np{Np} splits{splits}")
+    say(f"prefix Np{Np} splits{splits} waves{waves}")
     w = synth.small("prefix", B, Nq, H, D, 400 + Np, Np=Np, sigma_qk=2.0)
     q, kp, vp, kc, vc = w.tensors()
     ref = oracle.prefix_attention(q, kp, vp, kc, vc)
-    if splits == 0:
+    if splits == 0 and waves == 0:
         out = attn.prefix(dev(q), dev(kp) if Np else torch.empty(B, 0, H, D, dtype=torch.bfloat16,
                                                                   device="cuda"),
                           dev(vp) if Np else torch.empty(B, 0, H, D, dtype=torch.bfloat16,
@@ -77,7 +77,8 @@ def test_prefix_small_all_elements(Np, splits):
                           dev(kc), dev(vc))
         got = host(out)
     else:
-        got = run_ex(q, kp, vp, kc, vc, splits=splits) if Np else run_ex(q, kc, vc, splits=splits)
+        got = (run_ex(q, kp, vp, kc, vc, splits=splits, waves=waves) if Np
+               else run_ex(q, kc, vc, splits=splits, waves=waves))
     assert_accepted(got, ref, f"prefix Np{Np}")
 
 
@@ -95,8 +96,9 @@ def test_outlier_logits_small():
     w = synth.Workload("t", "dense", 2, 333, 4, 128, 600, sigma_qk=3.0, outliers=4)
     q, k, v = w.tensors()
     ref = oracle.attention(q, k, v)
-    for splits in (1, 5):
-        assert_accepted(run_ex(q, k, v, splits=splits), ref, f"outliers s{splits}")
+    for splits, waves in ((1, 0), (5, 0), (1, 8), (3, 8)):
+        assert_accepted(run_ex(q, k, v, splits=splits, waves=waves), ref,
+                        f"outliers s{splits} w{waves}")
 
 
 # ---------------------------------------------------------------- closed forms on the GPU

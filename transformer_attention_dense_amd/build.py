@@ -9,12 +9,16 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn_dense.so")
-SOURCES = [os.path.join(CSRC, "attn_kernels.hip"), os.path.join(CSRC, "attn_api.hip")]
+SOURCES = [os.path.join(CSRC, "attn_kernels.hip"), os.path.join(CSRC, "attn_pingpong.hip"),
+           os.path.join(CSRC, "attn_api.hip")]
 
 # Packed FP32 VALU forms are disabled for all device code: the compiler otherwise
 # emits them from ordinary float code.
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             # no NaN semantics are relied on (infinities are): lets max/min skip the
+             # canonicalisation of their inputs
+             "-fno-honor-nans",
              "-Wall", "-Wno-unused-command-line-argument"]
 
 

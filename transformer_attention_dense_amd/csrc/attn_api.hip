@@ -48,7 +48,8 @@ bool overlaps(const void* a, long long abytes, const void* b, long long bbytes) 
 int make_plan(int B, int Nq, int Nk, int H, int D, int num_splits, int waves, Plan* out) {
     if (B < 1 || Nq < 1 || Nk < 1 || H < 1) return ATTN_ERR_SHAPE;
     if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
-    if (num_splits < 0 || (waves != 0 && waves != 2 && waves != 4)) return ATTN_ERR_UNSUPPORTED;
+    if (num_splits < 0 || (waves != 0 && waves != 2 && waves != 4 && waves != 8))
+        return ATTN_ERR_UNSUPPORTED;
     // Offsets inside one batch of a tensor are formed in 32 bits before widening.
     if ((long long)Nq * H * D > kIndexLimit || (long long)Nk * H * D > kIndexLimit)
         return ATTN_ERR_OVERFLOW;
@@ -59,7 +60,16 @@ int make_plan(int B, int Nq, int Nk, int H, int D, int num_splits, int waves, Pl
     const int tile = attn::kKeyTile;
     const int key_tiles = (Nk + tile - 1) / tile;
     int w = waves;
-    if (w == 0) w = (Nq <= 64) ? 2 : 4;
+    if (w == 0) {
+        // The 8-wave ping-pong kernel (256 query rows per workgroup, one workgroup
+        // per CU) when it alone fills the 256 CUs; otherwise 2 or 4 waves, with the
+        // keys split below when needed.
+        const long long pp_blocks = (long long)((Nq + 255) / 256) * B * H;
+        if (Nq >= 256 && pp_blocks >= 256)
+            w = 8;
+        else
+            w = (Nq <= 64) ? 2 : 4;
+    }
     const int bm = 32 * w;
     const long long m_blocks = (Nq + bm - 1) / bm;
     const long long base = m_blocks * B * H;

@@ -1,0 +1,109 @@
+// Device-side building blocks shared by the attention forward kernels (gfx950).
+// Internal to the library; not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+#include <utility>
+
+namespace attn {
+namespace dev {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr float kRescaleLog2 = 8.0f;
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float wave_swap_max(float x) {
+    // max(x[lane], x[lane ^ 32]) for every lane
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                              false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float wave_swap_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                              false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Workgroup -> (query block, batch*head, split). Workgroups are dispatched to the
+// 8 XCDs round-robin by linear id; this remap gives each XCD a contiguous range of
+// (query block, head) work so the query blocks sharing one head's K/V run on the same
+// XCD and hit its L2.
+__device__ __forceinline__ void decode_workgroup(int m_blocks, int bh_count, int& mb, int& bh,
+                                                 int& split) {
+    const int L = blockIdx.x;
+    const int T = gridDim.x;
+    const int per = T >> 3;
+    const int L2 = (L < (per << 3)) ? (L & 7) * per + (L >> 3) : L;
+    mb = L2 % m_blocks;
+    const int rest = L2 / m_blocks;
+    bh = rest % bh_count;
+    split = rest / bh_count;
+}
+
+// Calls f(std::integral_constant<int, i>{}) for i = 0 .. N-1 (compile-time indices).
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+    (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// 16-byte global -> LDS copy (global_load_lds_dwordx4). Lane i of the wave writes
+// LDS bytes [dst + 16*i, dst + 16*i + 16); dst must be the same for the whole wave.
+__device__ __forceinline__ void load16_to_lds(const uint16_t* src, char* dst) {
+    typedef __attribute__((address_space(1))) void global_void;
+    typedef __attribute__((address_space(3))) void lds_void_t;
+    __builtin_amdgcn_global_load_lds((global_void*)(const_cast<uint16_t*>(src)),
+                                     (lds_void_t*)dst, 16, 0, 0);
+}
+
+// XOR swizzle of the 16-byte chunks of LDS row r (CPR chunks per row, period 16
+// rows). Chunk c of row r is stored at chunk position c ^ lds_swizzle(r). Chosen so
+// that (a) the 16 lanes of a K operand read (16 consecutive rows, one logical chunk)
+// hit 64 different banks, and (b) the 32 lanes of a V transpose read (4 consecutive
+// rows, 4 consecutive chunks) hit 64 different banks: the pattern keeps aligned
+// groups of 4 chunks together and moves whole groups between those rows.
+//   D = 128 (16 chunks, one row = all 64 banks): ((r & 3) << 2) | ((r >> 2) & 3)
+//   D = 64 (8 chunks, rows of one parity share a bank half): x = (r >> 1) & 7,
+//   ((x & 1) << 2) | ((x >> 1) & 3)
+template <int CPR>
+__device__ __forceinline__ int lds_swizzle(int r) {
+    if constexpr (CPR == 16) {
+        return ((r & 3) << 2) | ((r >> 2) & 3);
+    } else {
+        const int x = (r >> 1) & 7;
+        return ((x & 1) << 2) | ((x >> 1) & 3);
+    }
+}
+
+// Workgroup barrier that first waits until at most N of this wave's global->LDS
+// copies are outstanding and all of its LDS reads have returned. Unlike
+// __syncthreads(), later copies may stay in flight across the barrier. The empty asm
+// statements keep the compiler from moving memory accesses across it.
+template <int N>
+__device__ __forceinline__ void barrier_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+}
+
+}  // namespace dev
+}  // namespace attn

@@ -36,105 +36,13 @@
 #include <type_traits>
 #include <utility>
 
+#include "attn_device.h"
 #include "attn_launch.h"
 
 namespace attn {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-
-typedef __attribute__((address_space(3))) uint16_t lds_u16;
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-constexpr float kRescaleLog2 = 8.0f;
-constexpr int kWave = 64;
-
-__device__ __forceinline__ float wave_swap_max(float x) {
-    // max(x[lane], x[lane ^ 32]) for every lane
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                              false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-__device__ __forceinline__ float wave_swap_sum(float x) {
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                              false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// Workgroup -> (query block, batch*head, split). Workgroups are dispatched to the
-// 8 XCDs round-robin by linear id; this remap gives each XCD a contiguous range of
-// (query block, head) work so the query blocks sharing one head's K/V run on the same
-// XCD and hit its L2.
-__device__ __forceinline__ void decode_workgroup(int m_blocks, int bh_count, int& mb, int& bh,
-                                                 int& split) {
-    const int L = blockIdx.x;
-    const int T = gridDim.x;
-    const int per = T >> 3;
-    const int L2 = (L < (per << 3)) ? (L & 7) * per + (L >> 3) : L;
-    mb = L2 % m_blocks;
-    const int rest = L2 / m_blocks;
-    bh = rest % bh_count;
-    split = rest / bh_count;
-}
-
-// Calls f(std::integral_constant<int, i>{}) for i = 0 .. N-1 (compile-time indices).
-template <typename F, int... Is>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
-    (f(std::integral_constant<int, Is>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-    static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
-// 16-byte global -> LDS copy (global_load_lds_dwordx4). Lane i of the wave writes
-// LDS bytes [dst + 16*i, dst + 16*i + 16); dst must be the same for the whole wave.
-__device__ __forceinline__ void load16_to_lds(const uint16_t* src, char* dst) {
-    typedef __attribute__((address_space(1))) void global_void;
-    typedef __attribute__((address_space(3))) void lds_void_t;
-    __builtin_amdgcn_global_load_lds((global_void*)(const_cast<uint16_t*>(src)),
-                                     (lds_void_t*)dst, 16, 0, 0);
-}
-
-// XOR swizzle of the 16-byte chunks of LDS row r (CPR chunks per row, period 16
-// rows). Chunk c of row r is stored at chunk position c ^ lds_swizzle(r). Chosen so
-// that (a) the 16 lanes of a K operand read (16 consecutive rows, one logical chunk)
-// hit 64 different banks, and (b) the 32 lanes of a V transpose read (4 consecutive
-// rows, 4 consecutive chunks) hit 64 different banks: the pattern keeps aligned
-// groups of 4 chunks together and moves whole groups between those rows.
-//   D = 128 (16 chunks, one row = all 64 banks): ((r & 3) << 2) | ((r >> 2) & 3)
-//   D = 64 (8 chunks, rows of one parity share a bank half): x = (r >> 1) & 7,
-//   ((x & 1) << 2) | ((x >> 1) & 3)
-template <int CPR>
-__device__ __forceinline__ int lds_swizzle(int r) {
-    if constexpr (CPR == 16) {
-        return ((r & 3) << 2) | ((r >> 2) & 3);
-    } else {
-        const int x = (r >> 1) & 7;
-        return ((x & 1) << 2) | ((x >> 1) & 3);
-    }
-}
-
-// Workgroup barrier that first waits until at most N of this wave's global->LDS
-// copies are outstanding and all of its LDS reads have returned. Unlike
-// __syncthreads(), later copies may stay in flight across the barrier. The empty asm
-// statements keep the compiler from moving memory accesses across it.
-template <int N>
-__device__ __forceinline__ void barrier_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __asm__ volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
-    __builtin_amdgcn_s_barrier();
-    __asm__ volatile("" ::: "memory");
-}
+using namespace dev;
 
 template <int D, int NW, int BN>
 __global__ __launch_bounds__(NW* kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(FwdParams p) {
@@ -214,9 +122,12 @@ __global__ __launch_bounds__(NW* kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
             const long rowoff = (t0 < n0) ? (long)t0 * HD : (long)(t0 - n0) * HD;
             const uint16_t* base = ((t0 < n0) ? seg0 : seg1) + rowoff;
 #pragma unroll
-            for (int i = 0; i < PER_T; ++i)
-                load16_to_lds(base + (long)(i / NPAT) * NPAT * RSTEP * HD + ld_off[i % NPAT],
+            for (int i = 0; i < PER_T; ++i) {
+                const uint16_t* rb = base + (long)(i / NPAT) * NPAT * RSTEP * HD;  // uniform
+                load16_to_lds(reinterpret_cast<const uint16_t*>(
+                                  reinterpret_cast<const char*>(rb) + (unsigned)(2 * ld_off[i % NPAT])),
                               dst + i * NT * 16);
+            }
         } else {
             // ragged or segment-straddling tile: clamp rows into [t0, kend) and pick
             // the segment per row
@@ -434,13 +345,20 @@ __global__ __launch_bounds__(NW* kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
     if (active) qk_full(smem, sA);
     barrier_vmcnt<2 * PER_T>();  // K slot 0 is refilled during the first tile
 
-    auto step = [&](int t, const f32x16 (&sc)[NB], f32x16 (&sn)[NB]) {
+    // One tile of the steady state. J = t mod 6 is a compile-time constant, so the
+    // LDS slots (period 3) and the score buffers (period 2) fold into immediates.
+    auto step = [&](int t, auto jc) {
+        constexpr int J = decltype(jc)::value;
+        f32x16(&sc)[NB] = (J % 2 == 0) ? sA : sB;
+        f32x16(&sn)[NB] = (J % 2 == 0) ? sB : sA;
         const int t0 = kbeg + t * BN;
         const bool more_k = t + 3 < ntiles;
         const bool more_v = t + 2 < ntiles;
-        if (more_k) issue_k(t0 + 3 * BN, t % NSLOT);
-        if (more_v) issue_v(t0 + 2 * BN, (t + 2) % NSLOT);
-        if (active) tile_pipelined(sc, sn, kslot(t + 1), vslot(t));
+        if (more_k) issue_k(t0 + 3 * BN, J % NSLOT);
+        if (more_v) issue_v(t0 + 2 * BN, (J + 2) % NSLOT);
+        if (active)
+            tile_pipelined(sc, sn, smem + ((J + 1) % NSLOT) * TILEB,
+                           smem + (NSLOT + J % NSLOT) * TILEB);
         if (more_k)
             barrier_vmcnt<2 * PER_T>();
         else if (more_v)
@@ -448,16 +366,31 @@ __global__ __launch_bounds__(NW* kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
         else
             barrier_vmcnt<0>();
     };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    using I4 = std::integral_constant<int, 4>;
+    using I5 = std::integral_constant<int, 5>;
     int t = 0;
-    for (; t + 2 < ntiles; t += 2) {
-        step(t, sA, sB);
-        step(t + 1, sB, sA);
+    for (; t + 6 < ntiles; t += 6) {
+        step(t, I0{});
+        step(t + 1, I1{});
+        step(t + 2, I2{});
+        step(t + 3, I3{});
+        step(t + 4, I4{});
+        step(t + 5, I5{});
     }
-    if (t + 1 < ntiles) {
-        step(t, sA, sB);
-        if (active) tile_last(sB, kbeg + (t + 1) * BN, vslot(t + 1));
-    } else if (active) {
-        tile_last(sA, kbeg + t * BN, vslot(t));
+    // 0..5 more pipelined tiles, then the last tile (t is a multiple of 6 here)
+    const int rest = ntiles - 1 - t;
+    if (rest > 0) step(t, I0{});
+    if (rest > 1) step(t + 1, I1{});
+    if (rest > 2) step(t + 2, I2{});
+    if (rest > 3) step(t + 3, I3{});
+    if (rest > 4) step(t + 4, I4{});
+    if (active) {
+        const int tl = t + rest;
+        tile_last((rest % 2 == 0) ? sA : sB, kbeg + tl * BN, vslot(tl));
     }
 
     if (!active) return;
@@ -545,6 +478,7 @@ static hipError_t launch_fwd_t(const FwdParams& p, long long workgroups, hipStre
 
 hipError_t launch_fwd(int D, int waves, const FwdParams& p, long long workgroups,
                       hipStream_t stream) {
+    if (waves == 8) return launch_fwd_pingpong(D, p, workgroups, stream);
     if (D == 64 && waves == 4) return launch_fwd_t<64, 4>(p, workgroups, stream);
     if (D == 64 && waves == 2) return launch_fwd_t<64, 2>(p, workgroups, stream);
     if (D == 128 && waves == 4) return launch_fwd_t<128, 4>(p, workgroups, stream);

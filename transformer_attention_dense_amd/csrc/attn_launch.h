@@ -38,8 +38,12 @@ struct CombineParams {
 constexpr int key_tile(int D) { return D == 128 ? 32 : 64; }
 constexpr int kKeyTile = 64;
 
+// waves 2 or 4: attn_fwd_kernel (attn_kernels.hip); waves 8: the ping-pong kernel
+// (attn_pingpong.hip).
 hipError_t launch_fwd(int D, int waves, const FwdParams& p, long long workgroups,
                       hipStream_t stream);
+hipError_t launch_fwd_pingpong(int D, const FwdParams& p, long long workgroups,
+                               hipStream_t stream);
 hipError_t launch_combine(int D, const CombineParams& p, hipStream_t stream);
 
 }  // namespace attn

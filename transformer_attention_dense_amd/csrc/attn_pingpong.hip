@@ -1,0 +1,402 @@
+// Ping-pong attention forward kernel for MI355X (gfx950), for grids with many query
+// blocks. Same operation and data layout per wave as attn_fwd_kernel in
+// attn_kernels.hip (page "Audit SGLang interfaces and refresh validated kernel
+// solutions": the noncausal dense and prefix-cached attention definitions, FP32
+// accumulation, BF16 output), with a different schedule:
+//
+//   * A workgroup has 8 waves (256 query rows, 32 per wave) in two groups of 4; wave
+//     w and wave w + 4 share a SIMD. Every tile of 64 keys is processed in two
+//     phases per wave: G (MFMA: S(t) = K(t) Q^T and O += P(t-1) V(t-1)) and S
+//     (VALU: online softmax of S(t) into P(t)). Group 1 runs one phase behind group
+//     0, and all waves meet at one barrier per phase, so on every SIMD one wave
+//     issues MFMAs while the other works through the softmax.
+//   * K and V tiles stream global -> LDS (global_load_lds_dwordx4) into three-slot
+//     rings, two tiles ahead; the barrier before a tile's first use waits only for
+//     the copies it needs.
+//   * Tile phases are unrolled by 3 so the LDS slot of every access is a
+//     compile-time offset.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "attn_device.h"
+#include "attn_launch.h"
+
+namespace attn {
+namespace {
+
+using namespace dev;
+
+template <int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_pp_kernel(FwdParams p) {
+    static_assert(D == 64 || D == 128, "head dim");
+    constexpr int NW = 8;
+    constexpr int NT = NW * kWave;
+    constexpr int BN = 64;
+    constexpr int NB = BN / 32;            // 32-key blocks per tile
+    constexpr int KS = D / 16;             // MFMA k-steps over the head dim
+    constexpr int DB = D / 32;             // 32-wide head-dim blocks of O^T
+    constexpr int CPR = D / 8;             // 16-byte chunks per row
+    constexpr int ROWB = 2 * D;            // bytes per LDS row
+    constexpr int TILEB = BN * ROWB;       // bytes per K or V tile
+    constexpr int PER_T = BN * CPR / NT;   // 16-byte copies per thread per tensor per tile
+    constexpr int RSTEP = NT / CPR;        // rows per copy round
+    constexpr int NSLOT = 3;
+    constexpr int NQ = KS * NB;            // QK^T MFMAs per tile
+    constexpr int NP = 2 * NB * DB;        // PV MFMAs per tile
+    constexpr int NPAIR = NB * 8;          // exp pairs per lane per tile
+    static_assert(BN * CPR % NT == 0 && RSTEP % 16 == 0, "loader pattern");
+
+    __shared__ __attribute__((aligned(1024))) char smem[2 * NSLOT * TILEB];
+
+    int mb, bh, split;
+    decode_workgroup(p.m_blocks, p.B * p.H, mb, bh, split);
+    const int H = p.H;
+    const int b = bh / H;
+    const int h = bh - b * H;
+    const int HD = H * D;
+    const int n0 = p.n0;
+    const int nk = n0 + p.n1;
+    const int kbeg = split * p.keys_per_split;
+    const int kend = min(nk, kbeg + p.keys_per_split);
+    const int T = (kend - kbeg + BN - 1) / BN;
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int grp = wave >> 2;
+    const int lane = tid % kWave;
+    const int n = lane & 31;
+    const int g = lane >> 5;
+    const int q0 = mb * (NW * 32) + wave * 32;
+    const bool active = q0 < p.Nq;
+
+    const uint16_t* kseg0 = p.k0 + ((long)b * n0 * HD + (long)h * D);
+    const uint16_t* vseg0 = p.v0 + ((long)b * n0 * HD + (long)h * D);
+    const uint16_t* kseg1 = p.k1 ? p.k1 + ((long)b * p.n1 * HD + (long)h * D) : kseg0;
+    const uint16_t* vseg1 = p.v1 ? p.v1 + ((long)b * p.n1 * HD + (long)h * D) : vseg0;
+
+    // Q^T fragments (B operand): lane holds query n, dims 16*ks + 8g .. +7.
+    bf16x8 qf[KS];
+    {
+        const int qi = min(q0 + n, p.Nq - 1);
+        const uint16_t* qrow = p.q + ((long)(b * p.Nq + qi) * H + h) * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks + 8 * g);
+    }
+
+    // Loader: copy round i of thread tid fills physical chunk i*NT + tid of a tile:
+    // row r = (i*NT + tid) / CPR, chunk position tid % CPR holding logical chunk
+    // (tid % CPR) ^ swizzle(r). Rounds advance by RSTEP rows, a multiple of the
+    // swizzle period, so one per-lane offset serves every round.
+    const int ld_row0 = tid / CPR;
+    const int ld_off = ld_row0 * HD + ((tid % CPR) ^ lds_swizzle<CPR>(ld_row0)) * 8;
+    auto issue = [&](const uint16_t* seg0, const uint16_t* seg1, int t0, char* slot) {
+        char* const dst = slot + wave * kWave * 16;
+        const bool whole = (t0 + BN <= kend) && (t0 + BN <= n0 || t0 >= n0);
+        if (whole) {
+            const long rowoff = (t0 < n0) ? (long)t0 * HD : (long)(t0 - n0) * HD;
+            const uint16_t* base = ((t0 < n0) ? seg0 : seg1) + rowoff;
+#pragma unroll
+            for (int i = 0; i < PER_T; ++i) {
+                const uint16_t* rb = base + (long)i * RSTEP * HD;  // uniform
+                load16_to_lds(reinterpret_cast<const uint16_t*>(
+                                  reinterpret_cast<const char*>(rb) + (unsigned)(2 * ld_off)),
+                              dst + i * NT * 16);
+            }
+        } else {
+            // ragged or segment-straddling tile: clamp rows into [t0, kend) and pick
+            // the segment per row
+#pragma unroll
+            for (int i = 0; i < PER_T; ++i) {
+                const int r = ld_row0 + i * RSTEP;
+                const int key = min(t0 + r, kend - 1);
+                const int co = ld_off - ld_row0 * HD;
+                const uint16_t* src =
+                    key < n0 ? seg0 + (long)key * HD : seg1 + (long)(key - n0) * HD;
+                load16_to_lds(src + co, dst + i * NT * 16);
+            }
+        }
+    };
+    auto kslot = [&](int j) { return smem + j * TILEB; };
+    auto vslot = [&](int j) { return smem + (NSLOT + j) * TILEB; };
+    auto issue_k = [&](int t0, int slot) { issue(kseg0, kseg1, t0, kslot(slot)); };
+    auto issue_v = [&](int t0, int slot) { issue(vseg0, vseg1, t0, vslot(slot)); };
+
+    // Per-lane LDS byte offsets: K operand reads per k-step, V transpose reads per
+    // head-dim block and 8-key half.
+    int koff[KS];
+    {
+        const int tsw = lds_swizzle<CPR>(n) ^ g;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) koff[ks] = n * ROWB + 16 * ((2 * ks) ^ tsw);
+    }
+    int voff[DB][2];
+    {
+        const int tr_r = (lane & 15) >> 2;
+        const int tr_q = lane & 3;
+        const int half = (lane >> 4) & 1;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const int row = 8 * h2 + 4 * g + tr_r;
+                const int c = (4 * db + 2 * half + (tr_q >> 1)) ^ lds_swizzle<CPR>(row);
+                voff[db][h2] = row * ROWB + 16 * c + 8 * (tr_q & 1);
+            }
+    }
+
+    f32x16 o[DB];
+#pragma unroll
+    for (int i = 0; i < DB; ++i) o[i] = f32x16{};
+    f32x16 s[NB];       // scores of the tile between its G and S phases
+    bf16x8 pf[NB][2];   // probabilities of the tile between its S and next G phases
+    float m_ref = -INFINITY;
+    float l_part = 0.f;
+    const float c = p.c;
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+    auto read_k = [&](const char* kt, auto mc) {
+        constexpr int m = decltype(mc)::value;
+        return *reinterpret_cast<const bf16x8*>(kt + koff[m / NB] + (m % NB) * 32 * ROWB);
+    };
+    auto read_v = [&](const char* vt, auto jc) {
+        constexpr int j = decltype(jc)::value;
+        constexpr int cc = j / DB, kb = cc / 2, tt = cc % 2, db = j % DB;
+        constexpr int rowbase = (kb * 32 + 16 * tt) * ROWB;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(vt + voff[db][0] + rowbase));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(vt + voff[db][1] + rowbase));
+        const i16x8 a16 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        return __builtin_bit_cast(bf16x8, a16);
+    };
+
+    // G phase: MFMAs of S(t) (QK) and O += P(t-1) V(t-1) (PV), interleaved, with LDS
+    // operand fragments read three MFMAs ahead.
+    auto g_phase = [&](const char* kt, const char* vt, auto qk_c, auto pv_c) {
+        constexpr bool QK = decltype(qk_c)::value;
+        constexpr bool PV = decltype(pv_c)::value;
+        constexpr int NF = (QK ? NQ : 0) + (PV ? NP : 0);
+        // fragment f: with both, even f = QK m = f/2, odd f = PV j = f/2
+        auto is_qk = [](int f) { return QK && (!PV || (f % 2 == 0)); };
+        auto idx = [](int f) { return (QK && PV) ? f / 2 : f; };
+        bf16x8 fr[4];
+        auto read_f = [&](auto fc) {
+            constexpr int f = decltype(fc)::value;
+            if constexpr (is_qk(f))
+                fr[f % 4] = read_k(kt, std::integral_constant<int, idx(f)>{});
+            else
+                fr[f % 4] = read_v(vt, std::integral_constant<int, idx(f)>{});
+        };
+        __builtin_amdgcn_s_setprio(1);
+        read_f(std::integral_constant<int, 0>{});
+        read_f(std::integral_constant<int, 1>{});
+        read_f(std::integral_constant<int, 2>{});
+        static_for<NF>([&](auto fc) {
+            constexpr int f = decltype(fc)::value;
+            if constexpr (f + 3 < NF) read_f(std::integral_constant<int, f + 3>{});
+            if constexpr (is_qk(f)) {
+                constexpr int m = idx(f);
+                s[m % NB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    fr[f % 4], qf[m / NB], (m < NB) ? f32x16{} : s[m % NB], 0, 0, 0);
+            } else {
+                constexpr int j = idx(f);
+                constexpr int cc = j / DB, kb = cc / 2, tt = cc % 2, db = j % DB;
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[f % 4], pf[kb][tt], o[db], 0,
+                                                                0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        __builtin_amdgcn_s_setprio(0);
+    };
+
+    // S phase: online softmax of S(t) (tile starting at key t0) into P(t).
+    auto s_phase = [&](int t0) {
+        if (t0 + BN > kend) {
+#pragma unroll
+            for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = t0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+                    if (key >= kend) s[kb][r] = -INFINITY;
+                }
+        }
+        // row maximum: four independent chains, then one exchange with lane ^ 32
+        float m4[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) m4[k] = fmaxf(s[k / 2][8 * (k % 2)], s[k / 2][8 * (k % 2) + 1]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int r = 2; r < 8; r += 2)
+                m4[k] = fmaxf(fmaxf(m4[k], s[k / 2][8 * (k % 2) + r]), s[k / 2][8 * (k % 2) + r + 1]);
+        const float mx = wave_swap_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
+        const bool need = (mx - m_ref) * c > kRescaleLog2;
+        if (__builtin_amdgcn_ballot_w64(need) != 0) {
+            const float m_new = fmaxf(m_ref, mx);
+            const float alpha = (m_ref == -INFINITY) ? 0.f : exp2f((m_ref - m_new) * c);
+            l_part *= alpha;
+#pragma unroll
+            for (int i = 0; i < DB; ++i) o[i] *= alpha;
+            m_ref = m_new;
+        }
+        const float mc = (m_ref == -INFINITY) ? 0.f : m_ref * c;
+        float l2[2] = {0.f, 0.f};
+        static_for<NPAIR>([&](auto pc) {
+            constexpr int pi = decltype(pc)::value;
+            constexpr int cc = pi / 4, kb = cc / 2, tt = cc % 2, r = 8 * tt + 2 * (pi % 4);
+            const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -mc));
+            const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r + 1], c, -mc));
+            const bf16x2 pk = {(__bf16)e0, (__bf16)e1};
+            l2[pi % 2] = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, l2[pi % 2], false);
+            pf[kb][tt][r & 7] = pk[0];
+            pf[kb][tt][(r & 7) + 1] = pk[1];
+        });
+        l_part += l2[0] + l2[1];
+    };
+
+    using TRUE_ = std::true_type;
+    using FALSE_ = std::false_type;
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+
+    // ---- prologue: K(0), K(1), V(0) resident before phase 0
+    issue_k(kbeg, 0);
+    if (T > 1) issue_k(kbeg + BN, 1);
+    issue_v(kbeg, 0);
+    barrier_vmcnt<0>();
+
+    // Each group runs its own straight-line phase sequence; both execute the same
+    // barriers in the same order. Group 0: G(u) then S(u) in tile u; group 1: S(u-1)
+    // then G(u).
+    auto run = [&](auto grp_c) {
+        constexpr int GRP = decltype(grp_c)::value;
+        // phase 0 (tile 0): copies for K(2), V(1); group 0 computes S(0)
+        if (T > 2) issue_k(kbeg + 2 * BN, 2);
+        if (T > 1) issue_v(kbeg + BN, 1);
+        if (GRP == 0 && active) g_phase(kslot(0), vslot(0), TRUE_{}, FALSE_{});
+        barrier_vmcnt<63>();
+        // phase 1: group 0 softmax of tile 0, group 1 computes S(0)
+        if (active) {
+            if (GRP == 0)
+                s_phase(kbeg);
+            else
+                g_phase(kslot(0), vslot(0), TRUE_{}, FALSE_{});
+        }
+        // steady state: tile u in 1 .. T-1 (phases 2u and 2u+1); J = u mod 3
+        auto tile = [&](int u, auto jc) {
+            constexpr int J = decltype(jc)::value;
+            const int t0 = kbeg + u * BN;
+            // K(u) and V(u-1) were copied two phases ago; the copies of the last
+            // phase pair (K(u+1) if any, V(u)) may stay in flight.
+            if (u + 1 < T)
+                barrier_vmcnt<2 * PER_T>();
+            else
+                barrier_vmcnt<PER_T>();
+            if (u + 2 < T) issue_k(t0 + 2 * BN, (J + 2) % NSLOT);
+            if (u + 1 < T) issue_v(t0 + BN, (J + 1) % NSLOT);
+            if (active) {
+                if (GRP == 0)
+                    g_phase(kslot(J), vslot((J + 2) % NSLOT), TRUE_{}, TRUE_{});
+                else
+                    s_phase(t0 - BN);
+            }
+            barrier_vmcnt<63>();
+            if (active) {
+                if (GRP == 0)
+                    s_phase(t0);
+                else
+                    g_phase(kslot(J), vslot((J + 2) % NSLOT), TRUE_{}, TRUE_{});
+            }
+        };
+        int u = 1;
+        for (; u + 2 < T; u += 3) {
+            tile(u, I1{});
+            tile(u + 1, I2{});
+            tile(u + 2, I0{});
+        }
+        if (u < T) {
+            tile(u, I1{});
+            ++u;
+        }
+        if (u < T) {
+            tile(u, I2{});
+            ++u;
+        }
+        // tail (tile T): O += P(T-1) V(T-1)
+        barrier_vmcnt<0>();
+        const char* vlast = vslot((T - 1) % NSLOT);
+        if (active) {
+            if (GRP == 0)
+                g_phase(kslot(0), vlast, FALSE_{}, TRUE_{});
+            else
+                s_phase(kbeg + (T - 1) * BN);
+        }
+        barrier_vmcnt<63>();
+        if (GRP == 1 && active) g_phase(kslot(0), vlast, FALSE_{}, TRUE_{});
+    };
+    if (grp == 0)
+        run(I0{});
+    else
+        run(I1{});
+
+    if (!active) return;
+
+    // ---- epilogue
+    const float l_tot = wave_swap_sum(l_part);
+    const int qi = q0 + n;
+    if (p.splits == 1) {
+        const float inv = 1.0f / l_tot;
+        if (qi < p.Nq) {
+            uint16_t* orow = p.out + ((long)(b * p.Nq + qi) * H + h) * D;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    bf16x4 v;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = (__bf16)(o[db][4 * j + e] * inv);
+                    *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * j + 4 * g) = v;
+                }
+        }
+    } else {
+        const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+        if (qi < p.Nq) {
+            const long row = (long)(b * p.Nq + qi) * H + h;
+            const long rows = (long)p.B * p.Nq * H;
+            float* prow = p.part_o + ((long)split * rows + row) * D;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    f32x4 v;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = o[db][4 * j + e] * inv;
+                    *reinterpret_cast<f32x4*>(prow + 32 * db + 8 * j + 4 * g) = v;
+                }
+            if (g == 0) {
+                const float mref2 = (m_ref == -INFINITY) ? 0.f : m_ref * c;
+                p.part_lse[(long)split * rows + row] =
+                    l_tot > 0.f ? mref2 + __log2f(l_tot) : -INFINITY;
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_fwd_pingpong(int D, const FwdParams& p, long long workgroups,
+                               hipStream_t stream) {
+    if (D == 64)
+        hipLaunchKernelGGL(attn_fwd_pp_kernel<64>, dim3((unsigned)workgroups), dim3(512), 0,
+                           stream, p);
+    else if (D == 128)
+        hipLaunchKernelGGL(attn_fwd_pp_kernel<128>, dim3((unsigned)workgroups), dim3(512), 0,
+                           stream, p);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // namespace attn
