@@ -188,7 +188,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             else
                 fr[f % 4] = read_v(vt, std::integral_constant<int, idx(f)>{});
         };
-        __builtin_amdgcn_s_setprio(1);
         read_f(std::integral_constant<int, 0>{});
         read_f(std::integral_constant<int, 1>{});
         read_f(std::integral_constant<int, 2>{});
@@ -207,7 +206,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             }
             __builtin_amdgcn_sched_barrier(0);
         });
-        __builtin_amdgcn_s_setprio(0);
     };
 
     // S phase: online softmax of S(t) (tile starting at key t0) into P(t).
