@@ -13,7 +13,12 @@ Options beyond the common ones:
   --workload NAME   another workload from synth.WORKLOADS (parity sizes)
   --all             one JSON line per workload (no CPU baseline)
   --no-cpu          skip the CPU oracle timing
-  --copy-only MiB   run only a plain device copy of that size (counter calibration)
+  --calib-mib MiB   before the timed steps, run a plain streaming kernel (torch.neg on
+                    float32: reads and writes MiB each) `steps` times; rocprofv3 counter
+                    runs use it to calibrate FETCH_SIZE / WRITE_SIZE
+  --ingest F W      read two rocprofv3 --pmc CSVs (FETCH_SIZE run, WRITE_SIZE run) of a
+                    --calib-mib run and write profiles/traffic.json (HBM bytes per launch
+                    of the attention kernel, scaled by the calibration)
 """
 import argparse
 import hashlib
@@ -55,7 +60,8 @@ def parse():
     ap.add_argument("--all", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--copy-only", type=int, default=0)
+    ap.add_argument("--calib-mib", type=int, default=0)
+    ap.add_argument("--ingest", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     return ap.parse_args()
 
 
@@ -197,8 +203,58 @@ def record(w, r, steps, warmup, cpu):
     return rec
 
 
+def _counter_means(csv_path, counter):
+    """Mean counter value per dispatch for the attention kernels and the calibration
+    kernel of a rocprofv3 --pmc CSV."""
+    import csv
+    att, cal = [], []
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"]
+            if "attn_fwd" in name:
+                att.append(float(r["Counter_Value"]))
+            elif "neg" in name:
+                cal.append(float(r["Counter_Value"]))
+    if not att or not cal:
+        raise SystemExit(f"{csv_path}: missing attention or calibration dispatches for {counter}")
+    return sum(att) / len(att), sum(cal) / len(cal)
+
+
+def ingest(fetch_csv, write_csv, calib_mib, workload_name):
+    """FETCH_SIZE and WRITE_SIZE are in KiB per dispatch; each is scaled by what the same
+    counter reads for the calibration kernel, which moves exactly calib_mib MiB each way."""
+    known = calib_mib * 1024.0  # KiB
+    fa, fc = _counter_means(fetch_csv, "FETCH_SIZE")
+    wa, wc = _counter_means(write_csv, "WRITE_SIZE")
+    ff, wf = known / fc, known / wc
+    hbm = (fa * ff + wa * wf) * 1024.0
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        t = {}
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        t = {"kernel_source_hash": kernel_source_hash(), "workloads": {}}
+    t.setdefault("workloads", {})[workload_name] = {
+        "hbm_bytes_per_launch": round(hbm),
+        "fetch_kib_raw": fa, "write_kib_raw": wa,
+        "calibration": {"kib_each_way": known, "fetch_kib_read": fc, "write_kib_read": wc,
+                        "fetch_factor": ff, "write_factor": wf},
+    }
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(t, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps(t["workloads"][workload_name]))
+
+
 def main():
     args = parse()
+    if args.ingest:
+        ingest(args.ingest[0], args.ingest[1], args.calib_mib or 256, args.workload)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
               "(sharding across GPUs is described in the design notes, not built).",
@@ -212,15 +268,14 @@ def main():
         sys.exit(1)
     attn.library()  # fail loudly if the HIP library is missing
 
-    if args.copy_only:
-        n = args.copy_only * (1 << 20)
-        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    if args.calib_mib:
+        n = args.calib_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(max(1, args.steps)):
-            dst.copy_(src)
+            torch.neg(src, out=dst)
         torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes": n, "launches": max(1, args.steps)}))
-        return
+        del src, dst
 
     names = [w.name for w in synth.WORKLOADS] if args.all else [args.workload]
     for name in names:
