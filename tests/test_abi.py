@@ -106,8 +106,9 @@ def test_plan_for_the_workloads():
     assert p1["workspace_bytes"] == 0
     p3 = attn.attn_plan(1, 4096, 5120, 32, 128)
     assert p3["splits"] == 1 and p3["waves"] == 8 and p3["workgroups"] == 512
+    # D = 64 keeps two 4-wave workgroups per CU
     p2 = attn.attn_plan(2, 16384, 16384, 32, 64)
-    assert p2["waves"] == 8 and p2["workgroups"] == 64 * 64
+    assert p2["waves"] == 4 and p2["workgroups"] == 128 * 64
     # too few 256-row blocks: 4-wave workgroups; short sequences: 2 waves
     p0 = attn.attn_plan(1, 256, 256, 32, 64)
     assert p0["waves"] == 4

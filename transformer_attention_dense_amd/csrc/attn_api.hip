@@ -61,11 +61,12 @@ int make_plan(int B, int Nq, int Nk, int H, int D, int num_splits, int waves, Pl
     const int key_tiles = (Nk + tile - 1) / tile;
     int w = waves;
     if (w == 0) {
-        // The 8-wave ping-pong kernel (256 query rows per workgroup, one workgroup
-        // per CU) when it alone fills the 256 CUs; otherwise 2 or 4 waves, with the
+        // D = 128: the 8-wave ping-pong kernel (256 query rows per workgroup, one
+        // workgroup per CU) when it alone fills the 256 CUs. Otherwise, and for D = 64
+        // (where two 4-wave workgroups per CU measured faster), 2 or 4 waves, with the
         // keys split below when needed.
         const long long pp_blocks = (long long)((Nq + 255) / 256) * B * H;
-        if (Nq >= 256 && pp_blocks >= 256)
+        if (D == 128 && Nq >= 256 && pp_blocks >= 256)
             w = 8;
         else
             w = (Nq <= 64) ? 2 : 4;

@@ -67,10 +67,26 @@ __device__ __forceinline__ void static_for(F&& f) {
 // 16-byte global -> LDS copy (global_load_lds_dwordx4). Lane i of the wave writes
 // LDS bytes [dst + 16*i, dst + 16*i + 16); dst must be the same for the whole wave.
 __device__ __forceinline__ void load16_to_lds(const uint16_t* src, char* dst) {
-    typedef __attribute__((address_space(1))) void global_void;
-    typedef __attribute__((address_space(3))) void lds_void_t;
-    __builtin_amdgcn_global_load_lds((global_void*)(const_cast<uint16_t*>(src)),
-                                     (lds_void_t*)dst, 16, 0, 0);
+    // Issued as inline assembly on purpose: the compiler cannot tell which LDS bytes an
+    // LDS-DMA copy writes, so for the builtin it waits for every copy in flight before
+    // each later LDS read it cannot disambiguate (the transposed V reads), which would
+    // expose the memory latency of the prefetched tiles on every tile. The kernels order
+    // copies and reads themselves (barrier_vmcnt); hidden copies can only make the
+    // compiler's own vmcnt waits for other loads stricter, never looser.
+    // M0 holds the wave's LDS base; lane i writes bytes [16 i, 16 i + 16) above it.
+    const unsigned lds = __builtin_amdgcn_readfirstlane(
+        (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)dst);
+    // M0 is clobbered on purpose: nothing else in these kernels keeps a value in it.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+    __asm__ volatile(
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, off"
+        :
+        : "v"(src), "s"(lds)
+        : "memory", "m0");
+#pragma clang diagnostic pop
 }
 
 // XOR swizzle of the 16-byte chunks of LDS row r (CPR chunks per row, period 16
