@@ -9,6 +9,9 @@ Output: one JSON line (rank 0) with the metric, the roofline of the dominant ker
 (timed with HIP events on the stream the kernel is launched on) and the FP64 CPU
 oracle timed on a bounded sample of the same workload.
 
+Defaults: 2000 warmup steps (about half a second of work at the default workload: the
+GPU's clock needs that long under load to settle) and 500 timed steps.
+
 Options beyond the common ones:
   --workload NAME   another workload from synth.WORKLOADS (parity sizes)
   --all             one JSON line per workload (no CPU baseline)
@@ -54,8 +57,8 @@ def kernel_source_hash() -> str:
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--all", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
@@ -152,6 +155,14 @@ def bench_one(w, steps, warmup, torch, attn):
             "plan": plan, "finite": bool(torch.isfinite(out.float()).all())}
 
 
+def kernel_name(D, plan):
+    """The kernel(s) a launch of this plan runs (as rocprofv3 names them)."""
+    waves = plan["waves"]
+    main = (f"attn_fwd_pp_kernel<{D}>" if waves == 8 else
+            f"attn_fwd_kernel<{D}, {waves}, {32 if D == 128 else 64}>")
+    return main if plan["splits"] == 1 else main + f" + attn_combine_kernel<{D}>"
+
+
 def record(w, r, steps, warmup, cpu):
     ms_per_step = r["wall_s"] * 1000.0 / steps
     value = w.flop * steps / r["wall_s"] / 1e12
@@ -184,8 +195,7 @@ def record(w, r, steps, warmup, cpu):
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": hbm,
-            "kernel": "attn_fwd_kernel" + ("" if r["plan"]["splits"] == 1 else
-                                           " + attn_combine_kernel"),
+            "kernel": kernel_name(w.D, r["plan"]),
             "avg_launch_us": round(launch_us, 2),
             "algorithmic_flop_per_launch": w.flop,
             "algorithmic_bytes_per_launch": w.algorithmic_bytes,
