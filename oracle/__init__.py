@@ -19,7 +19,10 @@ prefix_cached_block_causal_h32_d128.json "reference"):
     O[b,i,h,:] = sum_j softmax_j( D**-0.5 * <Q[b,i,h,:], K[b,j,h,:]> ) * V[b,j,h,:]
 
 with K, V the concatenation (K_prefix, K_current), (V_prefix, V_current) for the
-prefix-cached operator. Inputs are BF16 bit patterns held in ``numpy.uint16``
+prefix-cached operator. The block-causal operator without prefix (same page,
+definitions/block_causal_attention/prefix_cached_block_causal_h32_d128_prefix0.json
+"reference") restricts row i's softmax to the keys j with j <= i or with the same
+nonnegative image id (image_ids [N], text = -1); see :func:`block_causal_rows`. Inputs are BF16 bit patterns held in ``numpy.uint16``
 arrays of layout [B, N, H, D]; outputs are unrounded FP64.
 """
 import ctypes
@@ -46,6 +49,8 @@ def _lib():
         L = ctypes.c_long
         lib.oracle_attn_rows.argtypes = [p, p, p, L, p, p, L, L, L, L, L, p, L, p, p, p,
                                          ctypes.c_double]
+        lib.oracle_block_causal_rows.restype = ctypes.c_int
+        lib.oracle_block_causal_rows.argtypes = [p, p, p, p, L, L, L, L, p, L, p, p, p]
         lib.oracle_num_threads.restype = ctypes.c_int
         _LIB = lib
     return _LIB
@@ -126,3 +131,50 @@ def prefix_attention(q, kp, vp, kc, vc, scale=None):
         return attention(q, kc, vc, scale=scale)
     return attention_rows(q, kp, vp, kc, vc, scale=scale).reshape(B, Nq, H, D)
 
+
+
+def _ids(image_ids, n):
+    ids = np.ascontiguousarray(np.asarray(image_ids), dtype=np.int32)
+    if ids.shape != (n,):
+        raise ValueError(f"image_ids: expected shape ({n},), got {ids.shape}")
+    return ids
+
+
+def block_causal_rows(q, k, v, image_ids, rows=None, want_lse=False, want_psum=False):
+    """FP64 block-causal attention (no prefix) for selected query rows.
+
+    q, k, v: [B, N, H, D] bits; image_ids: [N] int32 (text = -1). Row i sees key j
+    when j <= i, or when image_ids[i] >= 0 and image_ids[j] == image_ids[i].
+    rows: flat indices (b*N + i)*H + h, or None for every row. Returns out [rows, D].
+    """
+    q, k, v = _bits(q, "q"), _bits(k, "k"), _bits(v, "v")
+    B, N, H, D = q.shape
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError(f"k {k.shape} / v {v.shape} must match q {q.shape}")
+    ids = _ids(image_ids, N)
+    if rows is None:
+        nrows = B * N * H
+        rows_arr = None
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        nrows = rows_arr.size
+    out = np.empty((nrows, D), dtype=np.float64)
+    lse = np.empty(nrows, dtype=np.float64) if want_lse else None
+    psum = np.empty(nrows, dtype=np.float64) if want_psum else None
+    rc = _lib().oracle_block_causal_rows(_ptr(q), _ptr(k), _ptr(v), _ptr(ids), B, N, H, D,
+                                         _ptr(rows_arr), nrows, _ptr(out), _ptr(lse),
+                                         _ptr(psum))
+    if rc != 0:
+        raise RuntimeError(f"oracle_block_causal_rows failed with code {rc}")
+    res = [out]
+    if want_lse:
+        res.append(lse)
+    if want_psum:
+        res.append(psum)
+    return res[0] if len(res) == 1 else tuple(res)
+
+
+def block_causal_attention(q, k, v, image_ids):
+    """Block-causal attention (no prefix), full output [B, N, H, D] in FP64."""
+    B, N, H, D = q.shape
+    return block_causal_rows(q, k, v, image_ids).reshape(B, N, H, D)

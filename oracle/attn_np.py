@@ -8,7 +8,11 @@ definitions/dense_attention/noncausal_dense_attention_h32_d{64,128}.json: scores
 the bqhd,bkhd->bhqk contraction, times head_dim ** -0.5, softmax over keys, then the
 bhqk,bkhd->bqhd contraction with V. The prefix-cached operator
 (definitions/block_causal_attention/prefix_cached_block_causal_h32_d128.json) first
-concatenates prefix and current keys and values along the sequence axis.
+concatenates prefix and current keys and values along the sequence axis. The
+block-causal operator without prefix
+(definitions/block_causal_attention/prefix_cached_block_causal_h32_d128_prefix0.json)
+builds a boolean visibility matrix from positions and image ids, fills the hidden
+scores with -inf and takes the same softmax.
 """
 import numpy as np
 
@@ -25,8 +29,9 @@ def softmax_last(x: np.ndarray) -> np.ndarray:
     return e / np.sum(e, axis=-1, keepdims=True)
 
 
-def attention(q, k, v, scale=None):
-    """q [B,Nq,H,D], k/v [B,Nk,H,D] as BF16 bits or float arrays -> FP64 [B,Nq,H,D]."""
+def attention(q, k, v, scale=None, allowed=None):
+    """q [B,Nq,H,D], k/v [B,Nk,H,D] as BF16 bits or float arrays -> FP64 [B,Nq,H,D].
+    allowed: optional [Nq, Nk] boolean visibility (False -> score -inf)."""
     qf = bf16_bits_to_f64(q) if q.dtype == np.uint16 else np.asarray(q, np.float64)
     kf = bf16_bits_to_f64(k) if k.dtype == np.uint16 else np.asarray(k, np.float64)
     vf = bf16_bits_to_f64(v) if v.dtype == np.uint16 else np.asarray(v, np.float64)
@@ -34,6 +39,8 @@ def attention(q, k, v, scale=None):
     s = D ** -0.5 if scale is None else scale
     # [B,H,Nq,D] @ [B,H,D,Nk] -> [B,H,Nq,Nk]
     scores = np.matmul(qf.transpose(0, 2, 1, 3), kf.transpose(0, 2, 3, 1)) * s
+    if allowed is not None:
+        scores = np.where(allowed[None, None], scores, -np.inf)
     p = softmax_last(scores)
     # [B,H,Nq,Nk] @ [B,H,Nk,D] -> [B,H,Nq,D] -> [B,Nq,H,D]
     return np.matmul(p, vf.transpose(0, 2, 1, 3)).transpose(0, 2, 1, 3)
@@ -43,3 +50,15 @@ def prefix_attention(q, kp, vp, kc, vc, scale=None):
     """Keys cat(kp, kc) and values cat(vp, vc) along the sequence axis."""
     return attention(q, np.concatenate([kp, kc], axis=1), np.concatenate([vp, vc], axis=1),
                      scale=scale)
+
+
+def block_causal_visibility(image_ids) -> np.ndarray:
+    """[N, N] boolean: query i sees key j iff j <= i or both share an id >= 0."""
+    ids = np.asarray(image_ids, dtype=np.int64)
+    pos = np.arange(ids.size)
+    same_image = (ids[:, None] == ids[None, :]) & (ids[:, None] >= 0)
+    return (pos[None, :] <= pos[:, None]) | same_image
+
+
+def block_causal_attention(q, k, v, image_ids):
+    return attention(q, k, v, allowed=block_causal_visibility(image_ids))

@@ -15,6 +15,11 @@
  *     field "reference" (post-change text): keys and values are the concatenation
  *     along the sequence axis of (K_prefix, K_current) and (V_prefix, V_current);
  *     every query sees every key; scale 128 ** -0.5.
+ *   - definitions/block_causal_attention/prefix_cached_block_causal_h32_d128_prefix0.json,
+ *     field "reference" (post-change text): with positions 0..N-1 and image_ids [N]
+ *     (text = -1), query i may see key j when j <= i, or when image_ids[i] >= 0 and
+ *     image_ids[i] == image_ids[j]; the other scores are filled with -inf before the
+ *     softmax; scale 128 ** -0.5 (head_dim ** -0.5 here).
  * The pages evaluate in FP32; this oracle evaluates the same formula in FP64 and
  * returns the unrounded FP64 result (the pages' final BF16 cast is left to the
  * comparison).
@@ -125,6 +130,93 @@ int oracle_attn_rows(const uint16_t* q, const uint16_t* k0, const uint16_t* v0, 
             }
         }
         free(s);
+        free(qd);
+    }
+    return fail ? -fail : 0;
+}
+
+/*
+ * Block-causal attention without a prefix (the "_prefix0" definition): Q, K, V are
+ * [B, N, H, D] and ids is image_ids [N], shared by every batch entry. Only the
+ * allowed keys of a row enter its softmax (a -inf score contributes exp(-inf) = 0).
+ * Arguments and return codes as oracle_attn_rows (keys = queries, N of them);
+ * returns -4 if a row has no allowed key (cannot happen: j = i is always allowed).
+ */
+int oracle_block_causal_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                             const int32_t* ids, long B, long N, long H, long D,
+                             const long* rows, long nrows, double* out, double* lse,
+                             double* psum) {
+    if (!q || !k || !v || !ids || !out || B < 1 || N < 1 || H < 1 || D < 1) return -1;
+    const long total = B * N * H;
+    if (!rows) nrows = total;
+    const double scale = pow((double)D, -0.5);
+    int fail = 0;
+
+#pragma omp parallel
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)N);
+        unsigned char* allowed = (unsigned char*)malloc((size_t)N);
+        double* qd = (double*)malloc(sizeof(double) * (size_t)D);
+        if (!s || !allowed || !qd) {
+#pragma omp atomic write
+            fail = 3;
+        } else {
+#pragma omp for schedule(dynamic, 16)
+            for (long t = 0; t < nrows; ++t) {
+                const long r = rows ? rows[t] : t;
+                if (r < 0 || r >= total) {
+#pragma omp atomic write
+                    fail = 2;
+                    continue;
+                }
+                const long h = r % H;
+                const long bi = r / H;
+                const long i = bi % N;
+                const long b = bi / N;
+                const uint16_t* qr = q + ((b * N + i) * H + h) * D;
+                for (long d = 0; d < D; ++d) qd[d] = bf16_to_f64(qr[d]);
+
+                /* visibility of key j for query i, then the allowed scores */
+                double mx = -INFINITY;
+                long seen = 0;
+                for (long j = 0; j < N; ++j) {
+                    const int same_image = ids[i] >= 0 && ids[i] == ids[j];
+                    allowed[j] = (unsigned char)(j <= i || same_image);
+                    if (!allowed[j]) continue;
+                    ++seen;
+                    const uint16_t* kr = k + ((b * N + j) * H + h) * D;
+                    double dot = 0.0;
+                    for (long d = 0; d < D; ++d) dot += qd[d] * bf16_to_f64(kr[d]);
+                    s[j] = dot * scale;
+                    if (s[j] > mx) mx = s[j];
+                }
+                if (seen == 0) {
+#pragma omp atomic write
+                    fail = 4;
+                    continue;
+                }
+                double l = 0.0;
+                for (long j = 0; j < N; ++j) {
+                    if (!allowed[j]) continue;
+                    s[j] = exp(s[j] - mx);
+                    l += s[j];
+                }
+                double* o = out + t * D;
+                for (long d = 0; d < D; ++d) o[d] = 0.0;
+                double ps = 0.0;
+                for (long j = 0; j < N; ++j) {
+                    if (!allowed[j]) continue;
+                    const double p = s[j] / l;
+                    ps += p;
+                    const uint16_t* vr = v + ((b * N + j) * H + h) * D;
+                    for (long d = 0; d < D; ++d) o[d] += p * bf16_to_f64(vr[d]);
+                }
+                if (lse) lse[t] = mx + log(l);
+                if (psum) psum[t] = ps;
+            }
+        }
+        free(s);
+        free(allowed);
         free(qd);
     }
     return fail ? -fail : 0;
