@@ -74,6 +74,9 @@ def to_device(bits, torch):
 
 
 def make_call(w, dts, attn):
+    if w.kind == "block_causal":
+        out = attn.block_causal(*dts)
+        return out, (lambda: attn.block_causal(*dts, out=out))
     if w.kind == "dense":
         if w.Nk == w.Nq:
             out = attn.dense(*dts)
@@ -109,21 +112,32 @@ def cpu_baseline(w, seconds):
     t0 = time.perf_counter()
     while True:
         rows = np.arange(done, min(done + chunk, total_rows), dtype=np.int64)
-        oracle.attention_rows(ts[0], ts[1], ts[2], *ts[3:5], rows=rows)
+        if w.kind == "block_causal":
+            oracle.block_causal_rows(ts[0], ts[1], ts[2], ts[3], rows=rows)
+        else:
+            oracle.attention_rows(ts[0], ts[1], ts[2], *ts[3:5], rows=rows)
         done += rows.size
         el = time.perf_counter() - t0
         if el >= seconds or done >= total_rows:
             break
         chunk = min(chunk * 2, 8192)
-    rate = done * flop_per_row / el / 1e12
+    if w.kind == "block_causal":  # only the visible keys of the sampled rows
+        vis = w.visible_per_row()
+        rows_done = np.arange(done, dtype=np.int64)
+        rate = 4 * w.D * int(vis[(rows_done // w.H) % w.Nq].sum()) / el / 1e12
+    else:
+        rate = done * flop_per_row / el / 1e12
     return {"value": rate, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"{done} of {total_rows} query rows (first rows in [B,Nq,H] order) of "
-                      f"{w.name}, every key, FP64, {el:.1f} s"}
+                      f"{w.name}, every visible key, FP64, {el:.1f} s"}
 
 
 def bench_one(w, steps, warmup, torch, attn):
     ts = w.tensors()
-    dts = [to_device(t, torch) for t in ts]
+    if w.kind == "block_causal":  # Q, K, V bits and the int32 image ids
+        dts = [to_device(t, torch) for t in ts[:3]] + [torch.from_numpy(ts[3]).cuda()]
+    else:
+        dts = [to_device(t, torch) for t in ts]
     out, call = make_call(w, dts, attn)
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
@@ -150,7 +164,11 @@ def bench_one(w, steps, warmup, torch, attn):
         b.record(stream)
         b.synchronize()
         samples.append(a.elapsed_time(b) * 1000.0)
-    plan = attn.attn_plan(w.B, w.Nq, w.keys, w.H, w.D)
+    if w.kind == "block_causal":  # always one split of the 8-wave kernel
+        plan = {"splits": 1, "waves": 8, "workgroups": -(-w.Nq // 256) * w.B * w.H,
+                "workspace_bytes": 16 * -(-w.Nq // 32), "block_causal": True}
+    else:
+        plan = attn.attn_plan(w.B, w.Nq, w.keys, w.H, w.D)
     return {"wall_s": wall, "event_ms": ev_ms, "median_call_us": statistics.median(samples),
             "plan": plan, "finite": bool(torch.isfinite(out.float()).all())}
 
@@ -158,7 +176,9 @@ def bench_one(w, steps, warmup, torch, attn):
 def kernel_name(D, plan):
     """The kernel(s) a launch of this plan runs (as rocprofv3 names them)."""
     waves = plan["waves"]
-    main = (f"attn_fwd_pp_kernel<{D}>" if waves == 8 else
+    if plan.get("block_causal"):
+        return f"attn_bc_meta_kernel + attn_fwd_pp_kernel<{D}, true>"
+    main = (f"attn_fwd_pp_kernel<{D}, false>" if waves == 8 else
             f"attn_fwd_kernel<{D}, {waves}, {32 if D == 128 else 64}>")
     return main if plan["splits"] == 1 else main + f" + attn_combine_kernel<{D}>"
 

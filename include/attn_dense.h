@@ -79,7 +79,23 @@ int attn_cross(const void* q, const void* k, const void* v, void* out, int B, in
                int H, int D, void* stream);
 
 /*
- * General form behind the three calls above, with explicit launch options.
+ * Block-causal attention without a prefix (page "Audit SGLang interfaces and refresh
+ * validated kernel solutions",
+ * definitions/block_causal_attention/prefix_cached_block_causal_h32_d128_prefix0.json,
+ * post-change text; operand order Q, K_current, V_current, image_ids): query i sees
+ * key j when j <= i, or when image_ids[i] >= 0 and image_ids[j] == image_ids[i]
+ * (text tokens carry -1; the pages describe nonnegative ids as contiguous image
+ * blocks, but any ids are handled exactly). Scale D^-0.5.
+ * q, k, v: [B, N, H, D] BF16; image_ids: [N] int32 in device memory, shared by the
+ * batch, 16-byte aligned; out: [B, N, H, D] BF16, must overlap no input.
+ * Uses the library's per-device work space (16 bytes per 32 rows) for summaries of
+ * the ids; growing it synchronises the device, as for split-KV calls.
+ */
+int attn_block_causal(const void* q, const void* k, const void* v, const int* image_ids,
+                      void* out, int B, int N, int H, int D, void* stream);
+
+/*
+ * General form behind the dense, prefix and cross calls, with explicit launch options.
  * The keys are segment 0 (k0/v0, n0 rows) followed by segment 1 (k1/v1, n1 rows);
  * n0 + n1 >= 1, and a segment with zero rows may have NULL pointers.
  * num_splits: 0 = automatic, otherwise the number of key ranges computed in parallel

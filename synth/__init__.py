@@ -14,7 +14,13 @@ Generator: numpy ``Generator(PCG64(seed))``, ``standard_normal(dtype=float32)``
 times sigma, rounded to BF16 with round-to-nearest-even on the FP32 bit pattern.
 Seeds are ``1000 * (k + 1) + t`` for workload index k and tensor index t in call
 order (dense: Q=0, K=1, V=2; prefix: Q=0, K_prefix=1, V_prefix=2, K_current=3,
-V_current=4), so every tensor is reproducible on its own.
+V_current=4; block-causal: Q=0, K_current=1, V_current=2), so every tensor is
+reproducible on its own.
+
+Block-causal image ids follow the serving engine's segment list as the pages
+describe it (same page, the capture script's block-attention hook): text tokens
+-1, image segments numbered 0, 1, ... in order of appearance, each a contiguous
+block. A workload states its segments as (kind, length) pairs.
 """
 from dataclasses import dataclass, field
 from typing import Dict, List, Optional, Tuple
@@ -73,6 +79,8 @@ class Workload:
 
     kind "dense": Q [B,Nq,H,D], K/V [B,Nk,H,D] (Nk == Nq for self attention).
     kind "prefix": Q [B,Nq,H,D], K/V_prefix [B,Np,H,D], K/V_current [B,Nq,H,D].
+    kind "block_causal": Q, K_current, V_current [B,Nq,H,D] and image_ids [Nq] from
+    ``segments`` (a list of ("text" | "image", length) pairs summing to Nq).
     """
     name: str
     kind: str
@@ -86,12 +94,53 @@ class Workload:
     sigma_qk: float = 1.0
     outliers: int = 0     # channels per head scaled by outlier_factor in Q and K
     outlier_factor: float = 8.0
+    segments: Tuple[Tuple[str, int], ...] = ()
     description: str = ""
     extra: Dict = field(default_factory=dict)
 
     def __post_init__(self):
-        if self.kind == "dense" and self.Nk == 0:
+        if self.kind in ("dense", "block_causal") and self.Nk == 0:
             self.Nk = self.Nq
+        if self.kind == "block_causal":
+            if sum(n for _, n in self.segments) != self.Nq:
+                raise ValueError(f"{self.name}: segments do not add up to Nq={self.Nq}")
+
+    def image_ids(self) -> np.ndarray:
+        """int32 [Nq]: -1 for text, 0, 1, ... for the image segments in order."""
+        ids = np.empty(self.Nq, dtype=np.int32)
+        pos, nxt = 0, 0
+        for kind, n in self.segments:
+            if kind == "text":
+                ids[pos:pos + n] = -1
+            elif kind == "image":
+                ids[pos:pos + n] = nxt
+                nxt += 1
+            else:
+                raise ValueError(f"unknown segment kind {kind}")
+            pos += n
+        return ids
+
+    def visible_per_row(self) -> np.ndarray:
+        """int64 [Nq]: keys a block-causal query row sees (contiguous image blocks)."""
+        out = np.empty(self.Nq, dtype=np.int64)
+        pos = 0
+        for kind, n in self.segments:
+            out[pos:pos + n] = np.arange(pos + 1, pos + n + 1) if kind == "text" else pos + n
+            pos += n
+        return out
+
+    @property
+    def visible_pairs(self) -> int:
+        """Query-key pairs a block-causal call computes: a text row i sees i + 1 keys,
+        a row of an image block ending at e sees e keys (contiguous blocks)."""
+        total, pos = 0, 0
+        for kind, n in self.segments:
+            if kind == "text":
+                total += n * pos + n * (n + 1) // 2
+            else:
+                total += n * (pos + n)
+            pos += n
+        return total
 
     @property
     def keys(self) -> int:
@@ -99,11 +148,16 @@ class Workload:
 
     @property
     def flop(self) -> int:
-        """4*B*H*Nq*Nk*D: the two contractions (QK^T and PV), 2 FLOP per multiply-add."""
+        """4*B*H*Nq*Nk*D: the two contractions (QK^T and PV), 2 FLOP per multiply-add.
+        Block-causal: 4*B*H*D per visible query-key pair."""
+        if self.kind == "block_causal":
+            return 4 * self.B * self.H * self.D * self.visible_pairs
         return 4 * self.B * self.H * self.Nq * self.keys * self.D
 
     @property
     def exps(self) -> int:
+        if self.kind == "block_causal":
+            return self.B * self.H * self.visible_pairs
         return self.B * self.H * self.Nq * self.keys
 
     @property
@@ -111,14 +165,19 @@ class Workload:
         """Every input read once and the output written once, 2 bytes per element."""
         q = self.B * self.Nq * self.H * self.D
         kv = 2 * self.B * self.keys * self.H * self.D
-        return 2 * (q + kv + q)
+        ids = 4 * self.Nq if self.kind == "block_causal" else 0  # int32 image ids
+        return 2 * (q + kv + q) + ids
 
     def seed(self, t: int) -> int:
         return 1000 * (self.index + 1) + t
 
     def tensors(self) -> Tuple[np.ndarray, ...]:
-        """BF16 bit arrays in call order: (Q, K, V) or (Q, Kp, Vp, Kc, Vc)."""
+        """Arrays in call order: BF16 bits (Q, K, V) or (Q, Kp, Vp, Kc, Vc); block-causal
+        (Q, K_current, V_current, image_ids)."""
         B, Nq, H, D = self.B, self.Nq, self.H, self.D
+        if self.kind == "block_causal":
+            return tuple(normal_bf16((B, Nq, H, D), self.seed(t), self.sigma_qk if t < 2 else 1.0)
+                         for t in range(3)) + (self.image_ids(),)
         if self.kind == "dense":
             shapes = [(B, Nq, H, D), (B, self.Nk, H, D), (B, self.Nk, H, D)]
             qk = {0, 1}
@@ -163,6 +222,17 @@ WORKLOADS: List[Workload] = [
                          "outlier channels per head (same in Q and K) scaled x8, V ~ N(0,1)"),
 ]
 
+# Block-causal attention without prefix (the pages' "_prefix0" definition, 12 captured
+# workloads whose shapes the pages do not print): a text prompt, two images and text
+# around them; index 6 in the seeds.
+WORKLOADS.append(
+    Workload("block_causal_b1_n4096_h32_d128", "block_causal", 1, 4096, 32, 128, 6,
+             segments=(("text", 128), ("image", 1920), ("text", 64), ("image", 1920),
+                       ("text", 64)),
+             description="Block-causal attention without prefix, B=1 N=4096 H=32 D=128: "
+                         "text 128, image 1920, text 64, image 1920, text 64; N(0,1), "
+                         "scale 1/sqrt(128)"))
+
 BY_NAME = {w.name: w for w in WORKLOADS}
 
 
@@ -173,7 +243,7 @@ def workload(name_or_index) -> Workload:
 
 
 def small(kind: str, B: int, Nq: int, H: int, D: int, seed_base: int, Nk: Optional[int] = None,
-          Np: int = 0, sigma_qk: float = 1.0) -> Workload:
+          Np: int = 0, sigma_qk: float = 1.0, segments=()) -> Workload:
     """An ad-hoc seeded workload (tests); seed_base plays the role of the index k."""
     return Workload(f"{kind}_b{B}_nq{Nq}_h{H}_d{D}_s{seed_base}", kind, B, Nq, H, D,
-                    seed_base, Nk=Nk or 0, Np=Np, sigma_qk=sigma_qk)
+                    seed_base, Nk=Nk or 0, Np=Np, sigma_qk=sigma_qk, segments=tuple(segments))

@@ -132,3 +132,27 @@ def test_python_helpers_validate_before_the_library():
         attn.dense(x, x, x)  # CPU tensors are rejected
     with pytest.raises(TypeError):
         attn.dense(x.float(), x, x)
+
+
+def bc_call(q=A, k=A + 64 * MB, v=A + 128 * MB, ids=A + 192 * MB, out=A + 256 * MB, B=1, N=256,
+            H=32, D=128):
+    return attn.attn_block_causal(q, k, v, ids, out, B, N, H, D, None)
+
+
+def test_block_causal_rejects_bad_arguments():
+    assert bc_call(ids=None) == -1
+    assert bc_call(q=None) == -1 and bc_call(out=None) == -1
+    assert bc_call(N=0) == -2 and bc_call(B=0) == -2 and bc_call(H=-1) == -2
+    assert bc_call(D=96) == -3
+    assert bc_call(ids=A + 192 * MB + 4) == -4
+    assert bc_call(k=A + 64 * MB + 2) == -4
+    assert bc_call(out=A) == -5                     # output over q
+    assert bc_call(out=A + 192 * MB - 1024) == -5   # output over the image ids
+    assert bc_call(N=1 << 20, H=32) == -6
+
+
+def test_python_block_causal_validates_before_the_library():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 4, 1, 128, dtype=torch.bfloat16)
+    with pytest.raises((ValueError, TypeError)):
+        attn.block_causal(x, x, x, torch.zeros(4, dtype=torch.int32))

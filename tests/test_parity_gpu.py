@@ -101,6 +101,65 @@ def test_outlier_logits_small():
                         f"outliers s{splits} w{waves}")
 
 
+# ---------------------------------------------------------------- block-causal, every element
+
+def ids_from(segments):
+    return synth.small("block_causal", 1, sum(n for _, n in segments), 1, 64, 0,
+                       segments=segments).image_ids()
+
+
+BC_CASES = [
+    # B, N, H, D, image ids (name, array)
+    (2, 100, 2, 128, "text_image_text_image",
+     ids_from([("text", 10), ("image", 40), ("text", 5), ("image", 45)])),
+    (1, 200, 3, 64, "all_text_causal", np.full(200, -1, np.int32)),
+    (2, 130, 2, 128, "one_image_dense", np.zeros(130, np.int32)),
+    (1, 1, 2, 128, "single_token", np.full(1, -1, np.int32)),
+    (3, 33, 2, 64, "short_ragged", ids_from([("image", 20), ("text", 13)])),
+    (1, 700, 2, 128, "image_across_workgroups",
+     ids_from([("text", 50), ("image", 600), ("text", 50)])),
+    (1, 600, 2, 128, "images_back_to_back",
+     ids_from([("image", 200), ("image", 150), ("text", 3), ("image", 247)])),
+    (1, 300, 2, 64, "large_and_negative_ids",
+     np.array([-5] * 40 + [10 ** 6] * 100 + [-1] * 60 + [7] * 100, np.int32)),
+]
+
+
+@pytest.mark.parametrize("B,N,H,D,name,ids", BC_CASES, ids=[c[4] for c in BC_CASES])
+def test_block_causal_small_all_elements(B, N, H, D, name, ids):
+    say(f"block-causal {name} B{B} N{N} H{H} D{D}")
+    w = synth.small("dense", B, N, H, D, 1100 + N, sigma_qk=2.0)
+    q, k, v = w.tensors()
+    ref = oracle.block_causal_attention(q, k, v, ids)
+    got = host(attn.block_causal(dev(q), dev(k), dev(v), torch.from_numpy(ids).cuda()))
+    assert_accepted(got, ref, f"block-causal {name}")
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_block_causal_arbitrary_ids(seed):
+    """Ids that are not contiguous blocks (the same id in separate runs): the kernel
+    evaluates the definition exactly, not a per-row key bound."""
+    rng = np.random.default_rng(seed)
+    B, N, H, D = 1, 333, 2, 128
+    ids = rng.integers(-1, 5, size=N).astype(np.int32)
+    w = synth.small("dense", B, N, H, D, 1200 + seed, sigma_qk=2.0)
+    q, k, v = w.tensors()
+    ref = oracle.block_causal_attention(q, k, v, ids)
+    got = host(attn.block_causal(dev(q), dev(k), dev(v), torch.from_numpy(ids).cuda()))
+    assert_accepted(got, ref, f"block-causal arbitrary ids {seed}")
+
+
+def test_block_causal_extremes_match_other_calls():
+    """All one image equals dense attention; the same GPU inputs through both calls."""
+    B, N, H, D = 1, 512, 2, 128
+    w = synth.small("dense", B, N, H, D, 1300, sigma_qk=2.0)
+    tq, tk, tv = (dev(t) for t in w.tensors())
+    a = host(attn.block_causal(tq, tk, tv, torch.zeros(N, dtype=torch.int32, device="cuda")))
+    b = host(attn.dense(tq, tk, tv))
+    # two GPU paths (different kernels and tile sizes) under the acceptance rule
+    assert_accepted(a, bf16_bits_to_f64(b), "block-causal one image vs dense")
+
+
 # ---------------------------------------------------------------- closed forms on the GPU
 
 def test_identical_keys_give_mean_of_values():
@@ -179,28 +238,31 @@ def test_workload_full_size(idx):
     say(f"workload {w.name}: generating inputs")
     ts = w.tensors()
     say(f"workload {w.name}: GPU call")
-    dts = [dev(t) for t in ts]
+    if w.kind == "block_causal":
+        dts = [dev(t) for t in ts[:3]] + [torch.from_numpy(ts[3]).cuda()]
+        out = attn.block_causal(*dts)
+    else:
+        dts = [dev(t) for t in ts]
     if w.kind == "dense":
         out = attn.dense(*dts) if w.Nk == w.Nq else attn.cross(*dts)
-    else:
+    elif w.kind == "prefix":
         out = attn.prefix(*dts)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(out.float()).all())
     # convex combination: every output lies within the per-(b, h, d) range of V
-    vs = [dts[2]] if w.kind == "dense" else [dts[2], dts[4]]
+    vs = [dts[2]] if w.kind != "prefix" else [dts[2], dts[4]]
     vmin = torch.stack([x.float().amin(dim=1) for x in vs]).amin(0)
     vmax = torch.stack([x.float().amax(dim=1) for x in vs]).amax(0)
     o = out.float()
     assert bool((o >= vmin[:, None] - 1e-2).all()) and bool((o <= vmax[:, None] + 1e-2).all())
     got = host(out).reshape(-1, w.D)
     say(f"workload {w.name}: oracle rows")
-    if w.B * w.Nq * w.H * w.keys * w.D <= (1 << 30):
-        rows = None
-        ref = oracle.attention_rows(ts[0], ts[1], ts[2], *ts[3:5])
-        sel = got
+    rows = None if w.B * w.Nq * w.H * w.keys * w.D <= (1 << 30) else \
+        sample_rows(w, 1500, 800 + idx)
+    if w.kind == "block_causal":
+        ref = oracle.block_causal_rows(ts[0], ts[1], ts[2], ts[3], rows=rows)
     else:
-        rows = sample_rows(w, 1500, 800 + idx)
         ref = oracle.attention_rows(ts[0], ts[1], ts[2], *ts[3:5], rows=rows)
-        sel = got[rows]
+    sel = got if rows is None else got[rows]
     res = assert_accepted(sel, ref, w.name)
     say(f"workload {w.name}: {res}")

@@ -35,8 +35,8 @@ ERRORS = {
 }
 
 # Exported symbols, in header order.
-SYMBOLS = ("attn_dense", "attn_prefix", "attn_cross", "attn_fwd_ex", "attn_plan",
-           "attn_reserve_workspace", "attn_strerror", "attn_abi_version")
+SYMBOLS = ("attn_dense", "attn_prefix", "attn_cross", "attn_block_causal", "attn_fwd_ex",
+           "attn_plan", "attn_reserve_workspace", "attn_strerror", "attn_abi_version")
 
 
 class AttnError(RuntimeError):
@@ -61,6 +61,7 @@ def library() -> ctypes.CDLL:
     lib.attn_dense.argtypes = [p, p, p, p, i, i, i, i, p]
     lib.attn_prefix.argtypes = [p, p, p, p, p, p, i, i, i, i, i, p]
     lib.attn_cross.argtypes = [p, p, p, p, i, i, i, i, i, p]
+    lib.attn_block_causal.argtypes = [p, p, p, p, p, i, i, i, i, p]
     lib.attn_fwd_ex.argtypes = [p, p, p, i, p, p, i, p, i, i, i, i, i, i, p]
     lib.attn_plan.argtypes = [i, i, i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i),
                               ctypes.POINTER(ll), ctypes.POINTER(ll)]
@@ -87,6 +88,10 @@ def attn_prefix(q, kp, vp, kc, vc, out, B, Nq, Np, H, D, stream=0) -> int:
 
 def attn_cross(q, k, v, out, B, Nq, Nk, H, D, stream=0) -> int:
     return library().attn_cross(q, k, v, out, B, Nq, Nk, H, D, stream)
+
+
+def attn_block_causal(q, k, v, image_ids, out, B, N, H, D, stream=0) -> int:
+    return library().attn_block_causal(q, k, v, image_ids, out, B, N, H, D, stream)
 
 
 def attn_fwd_ex(q, k0, v0, n0, k1, v1, n1, out, B, Nq, H, D, num_splits=0, waves=0,
@@ -203,6 +208,28 @@ def prefix(q, kp, vp, kc, vc, out=None):
                      Nq, Np, H, D, _stream(q))
     if rc != ATTN_OK:
         raise AttnError(rc, "attn_prefix")
+    return out
+
+
+def block_causal(q, k, v, image_ids, out=None):
+    """Block-causal attention without prefix in the pages' operand order (Q, K_current,
+    V_current, image_ids): row i sees key j when j <= i or when both carry the same
+    nonnegative image id. image_ids: int32 [N] on the same GPU (text = -1)."""
+    import torch
+    _check(q, "q")
+    B, N, H, D = q.shape
+    _check(k, "k_current", q.shape)
+    _check(v, "v_current", q.shape)
+    if not isinstance(image_ids, torch.Tensor) or image_ids.dtype != torch.int32:
+        raise TypeError("image_ids must be an int32 torch.Tensor")
+    if image_ids.device != q.device or tuple(image_ids.shape) != (N,) or \
+            not image_ids.is_contiguous():
+        raise ValueError(f"image_ids must be a contiguous [{N}] tensor on {q.device}")
+    out = _out(q, out)
+    rc = attn_block_causal(q.data_ptr(), k.data_ptr(), v.data_ptr(), image_ids.data_ptr(),
+                           out.data_ptr(), B, N, H, D, _stream(q))
+    if rc != ATTN_OK:
+        raise AttnError(rc, "attn_block_causal")
     return out
 
 

@@ -185,6 +185,8 @@ int run(const void* q, const void* k0, const void* v0, int n0, const void* k1, c
     p.splits = plan.splits;
     p.m_blocks = plan.m_blocks;
     p.c = (float)(pow((double)D, -0.5) * 1.4426950408889634);  // D^-0.5 * log2(e)
+    p.ids = nullptr;
+    p.meta = nullptr;
 
     if (attn::launch_fwd(D, plan.waves, p, plan.workgroups, st) != hipSuccess)
         return ATTN_ERR_HIP;
@@ -200,9 +202,62 @@ int run(const void* q, const void* k0, const void* v0, int n0, const void* k1, c
     return ATTN_OK;
 }
 
+// Block-causal attention without prefix: keys are the queries' own positions.
+int run_block_causal(const void* q, const void* k, const void* v, const int* ids, void* out,
+                     int B, int N, int H, int D, void* stream) {
+    if (!q || !k || !v || !ids || !out) return ATTN_ERR_NULL;
+    Plan plan;
+    const int rc = make_plan(B, N, N, H, D, 1, 8, &plan);  // one key split, ping-pong
+    if (rc != ATTN_OK) return rc;
+    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(ids) || misaligned(out))
+        return ATTN_ERR_ALIGN;
+    const long long bytes = 2LL * B * N * H * D;
+    const long long idbytes = 4LL * N;
+    if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) ||
+        overlaps(out, bytes, v, bytes) || overlaps(out, bytes, ids, idbytes))
+        return ATTN_ERR_ALIAS;
+
+    // ---- device work from here on: per-row-block id summaries in the work space
+    const long long nblk = (N + attn::kMetaRows - 1) / attn::kMetaRows;
+    void* ws = nullptr;
+    const int wrc = reserve(nblk * 16, &ws);
+    if (wrc != ATTN_OK) return wrc;
+    const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    attn::FwdParams p;
+    p.q = static_cast<const uint16_t*>(q);
+    p.k0 = static_cast<const uint16_t*>(k);
+    p.v0 = static_cast<const uint16_t*>(v);
+    p.k1 = nullptr;
+    p.v1 = nullptr;
+    p.n0 = N;
+    p.n1 = 0;
+    p.out = static_cast<uint16_t*>(out);
+    p.part_o = nullptr;
+    p.part_lse = nullptr;
+    p.B = B;
+    p.Nq = N;
+    p.H = H;
+    p.keys_per_split = plan.keys_per_split;
+    p.splits = 1;
+    p.m_blocks = plan.m_blocks;
+    p.c = (float)(pow((double)D, -0.5) * 1.4426950408889634);
+    p.ids = ids;
+    p.meta = static_cast<int*>(ws);
+    if (attn::launch_bc_meta(ids, N, static_cast<int*>(ws), st) != hipSuccess)
+        return ATTN_ERR_HIP;
+    if (attn::launch_fwd_block_causal(D, p, plan.workgroups, st) != hipSuccess)
+        return ATTN_ERR_HIP;
+    return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int attn_block_causal(const void* q, const void* k, const void* v, const int* image_ids,
+                      void* out, int B, int N, int H, int D, void* stream) {
+    return run_block_causal(q, k, v, image_ids, out, B, N, H, D, stream);
+}
 
 int attn_dense(const void* q, const void* k, const void* v, void* out, int B, int N, int H,
                int D, void* stream) {

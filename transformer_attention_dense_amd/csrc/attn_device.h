@@ -42,12 +42,24 @@ __device__ __forceinline__ float wave_swap_sum(float x) {
 // 8 XCDs round-robin by linear id; this remap gives each XCD a contiguous range of
 // (query block, head) work so the query blocks sharing one head's K/V run on the same
 // XCD and hit its L2.
+//
+// heavy_last_blocks (causal-like masks, where later query blocks see more keys): within
+// each XCD's share, hand out query blocks from the last to the first, cycling over the
+// share's heads, so the longest workgroups start first (the share keeps its heads, so
+// their K/V stay in that XCD's L2).
 __device__ __forceinline__ void decode_workgroup(int m_blocks, int bh_count, int& mb, int& bh,
-                                                 int& split) {
+                                                 int& split, bool heavy_last_blocks = false) {
     const int L = blockIdx.x;
     const int T = gridDim.x;
     const int per = T >> 3;
-    const int L2 = (L < (per << 3)) ? (L & 7) * per + (L >> 3) : L;
+    int L2 = (L < (per << 3)) ? (L & 7) * per + (L >> 3) : L;
+    if (heavy_last_blocks && L < (per << 3) && per % m_blocks == 0) {
+        const int hx = per / m_blocks;  // heads in this XCD's share
+        const int r = L2 % per;
+        L2 = (L2 - r) + (r % hx) * m_blocks + (m_blocks - 1 - r / hx);
+    } else if (heavy_last_blocks) {
+        L2 = (L2 / m_blocks) * m_blocks + (m_blocks - 1 - L2 % m_blocks);
+    }
     mb = L2 % m_blocks;
     const int rest = L2 / m_blocks;
     bh = rest % bh_count;

@@ -23,7 +23,16 @@ struct FwdParams {
     int splits;
     int m_blocks;  // query blocks per (batch, head)
     float c;       // D^-0.5 * log2(e)
+    // Block-causal visibility (null for full visibility): image ids [Nq] (keys are
+    // the queries' own positions) and per-32-row block summaries of them (bc_meta).
+    const int* ids;
+    const int* meta;
 };
+
+// Summary of the image ids of rows [32 b, 32 b + 32) of a block-causal call, four
+// ints per block: smallest and largest nonnegative id (INT_MAX / -1 when there is
+// none), number of negative (text) ids, and 0.
+constexpr int kMetaRows = 32;
 
 struct CombineParams {
     const float* part_o;
@@ -44,6 +53,11 @@ hipError_t launch_fwd(int D, int waves, const FwdParams& p, long long workgroups
                       hipStream_t stream);
 hipError_t launch_fwd_pingpong(int D, const FwdParams& p, long long workgroups,
                                hipStream_t stream);
+// Block-causal attention: the ping-pong kernel with per-tile visibility (p.ids and
+// p.meta set, one key split), after launch_bc_meta has filled p.meta.
+hipError_t launch_fwd_block_causal(int D, const FwdParams& p, long long workgroups,
+                                   hipStream_t stream);
+hipError_t launch_bc_meta(const int* ids, int n, int* meta, hipStream_t stream);
 hipError_t launch_combine(int D, const CombineParams& p, hipStream_t stream);
 
 }  // namespace attn

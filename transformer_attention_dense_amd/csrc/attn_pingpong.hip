@@ -26,7 +26,45 @@ namespace {
 
 using namespace dev;
 
-template <int D>
+// Block-causal visibility (page "Audit SGLang interfaces and refresh validated kernel
+// solutions", definitions/block_causal_attention/
+// prefix_cached_block_causal_h32_d128_prefix0.json): query i sees key j when j <= i,
+// or when image_ids[i] >= 0 and image_ids[j] == image_ids[i].
+//
+// End (exclusive) of the keys rows [qa, qb] may see: every key up to qb, plus the
+// 64-key tiles after qb whose range of nonnegative ids overlaps the rows' range
+// (conservative; the per-element mask decides). Lane-parallel over tiles, the result
+// is uniform across the wave.
+__device__ int bc_key_end(const int* meta, int n, int qa, int qb, int lane) {
+    int qmin = 0x7fffffff, qmax = -1;
+    for (int blk = qa / kMetaRows; blk <= qb / kMetaRows; ++blk) {
+        qmin = min(qmin, meta[4 * blk]);
+        qmax = max(qmax, meta[4 * blk + 1]);
+    }
+    const int end = qb + 1;
+    if (qmax < 0) return end;  // only text rows: causal
+    const int nblk = (n + kMetaRows - 1) / kMetaRows;
+    const int tiles = (n + 63) / 64;
+    const int first = qb / 64 + 1;  // first tile that starts after row qb
+    for (int base = first + ((tiles - first - 1) / 64) * 64; base >= first; base -= 64) {
+        const int tt = base + lane;
+        bool hit = false;
+        if (tt < tiles) {
+            const int b0 = 2 * tt, b1 = min(2 * tt + 1, nblk - 1);
+            const int kmin = min(meta[4 * b0], meta[4 * b1]);
+            const int kmax = max(meta[4 * b0 + 1], meta[4 * b1 + 1]);
+            hit = kmax >= qmin && kmin <= qmax;
+        }
+        const unsigned long long m = __builtin_amdgcn_ballot_w64(hit);
+        if (m) {
+            const int top = base + 63 - __builtin_clzll(m);
+            return max(end, min(n, 64 * top + 64));
+        }
+    }
+    return end;
+}
+
+template <int D, bool BC>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_pp_kernel(FwdParams p) {
     static_assert(D == 64 || D == 128, "head dim");
     constexpr int NW = 8;
@@ -49,7 +87,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __shared__ __attribute__((aligned(1024))) char smem[2 * NSLOT * TILEB];
 
     int mb, bh, split;
-    decode_workgroup(p.m_blocks, p.B * p.H, mb, bh, split);
+    decode_workgroup(p.m_blocks, p.B * p.H, mb, bh, split, BC);
     const int H = p.H;
     const int b = bh / H;
     const int h = bh - b * H;
@@ -57,17 +95,35 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int n0 = p.n0;
     const int nk = n0 + p.n1;
     const int kbeg = split * p.keys_per_split;
-    const int kend = min(nk, kbeg + p.keys_per_split);
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    // block-causal: the keys of this workgroup's rows stop at their last visible tile
+    // (one key split)
+    const int kend =
+        BC ? min(nk, bc_key_end(p.meta, p.Nq, mb * (NW * 32), min(mb * (NW * 32) + NW * 32 - 1,
+                                                                   p.Nq - 1), lane))
+           : min(nk, kbeg + p.keys_per_split);
     const int T = (kend - kbeg + BN - 1) / BN;
 
-    const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int grp = wave >> 2;
-    const int lane = tid % kWave;
     const int n = lane & 31;
     const int g = lane >> 5;
     const int q0 = mb * (NW * 32) + wave * 32;
     const bool active = q0 < p.Nq;
+    // block-causal: this lane's query image id, and whether the wave's 32 rows all
+    // carry one nonnegative id (then a tile of keys with only that id is fully visible)
+    int idq = -1, wq_id = -1, wq_max = -1;
+    bool wq_uniform = false;
+    if constexpr (BC) {
+        idq = p.ids[min(q0 + n, p.Nq - 1)];
+        if (active) {
+            const int* wm = p.meta + 4 * (q0 / kMetaRows);
+            wq_uniform = wm[2] == 0 && wm[0] == wm[1];
+            wq_id = wm[0];   // smallest nonnegative id of the rows
+            wq_max = wm[1];  // largest (-1: text rows only)
+        }
+    }
 
     const uint16_t* kseg0 = p.k0 + ((long)b * n0 * HD + (long)h * D);
     const uint16_t* vseg0 = p.v0 + ((long)b * n0 * HD + (long)h * D);
@@ -209,8 +265,66 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     };
 
     // S phase: online softmax of S(t) (tile starting at key t0) into P(t).
-    auto s_phase = [&](int t0) {
-        if (t0 + BN > kend) {
+    // Block-causal mask of the tile at key t0 (keys >= kend hidden as well). Skipped
+    // when every key of the tile is visible to every row of the wave: the tile lies
+    // at or below the wave's first row, or keys and rows all carry the same image id.
+    // Returns false when no key of the tile is visible to any row of the wave (every
+    // key after the wave's last row, and no image id shared with the rows): the caller
+    // then sets the probabilities to zero without computing them.
+    auto bc_mask = [&](int t0) __attribute__((always_inline)) {
+        const bool whole = t0 + BN <= kend;
+        bool full = whole && t0 + BN - 1 <= q0;
+        if (!full) {
+            const int nblk = (p.Nq + kMetaRows - 1) / kMetaRows;
+            const int* km0 = p.meta + 4 * (t0 / kMetaRows);  // the tile's two row blocks
+            const int* km1 = p.meta + 4 * min(t0 / kMetaRows + 1, nblk - 1);
+            if (t0 > q0 + 31) {
+                const int kmin = min(km0[0], km1[0]), kmax = max(km0[1], km1[1]);
+                if (wq_max < 0 || kmax < wq_id || kmin > wq_max) return false;
+            }
+            if (whole && wq_uniform)
+                full = km0[2] == 0 && km1[2] == 0 && km0[0] == wq_id && km0[1] == wq_id &&
+                       km1[0] == wq_id && km1[1] == wq_id;
+        }
+        if (full) return true;
+        const int i = q0 + n;
+#pragma unroll
+        for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                // registers 4 q4 .. 4 q4 + 3 hold keys j0 .. j0 + 3
+                const int j0 = t0 + kb * 32 + 8 * q4 + 4 * g;
+                int idk[4];
+                if (j0 + 3 < p.Nq) {
+                    const int4 v4 = *reinterpret_cast<const int4*>(p.ids + j0);
+                    idk[0] = v4.x;
+                    idk[1] = v4.y;
+                    idk[2] = v4.z;
+                    idk[3] = v4.w;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) idk[e] = p.ids[min(j0 + e, p.Nq - 1)];
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int j = j0 + e;
+                    const bool vis = j < kend && (j <= i || (idq >= 0 && idk[e] == idq));
+                    if (!vis) s[kb][4 * q4 + e] = -INFINITY;
+                }
+            }
+        return true;
+    };
+
+    auto s_phase = [&](int t0) __attribute__((always_inline)) {
+        if constexpr (BC) {
+            if (!bc_mask(t0)) {  // nothing visible: P = 0, running max and sums unchanged
+#pragma unroll
+                for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+                    for (int tt = 0; tt < 2; ++tt) pf[kb][tt] = bf16x8{};
+                return;
+            }
+        } else if (t0 + BN > kend) {
 #pragma unroll
             for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
@@ -382,18 +496,64 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
 }
 
+// One thread per block of kMetaRows image ids: smallest and largest nonnegative id
+// and the number of negative (text) ids.
+__global__ void attn_bc_meta_kernel(const int* ids, int n, int* meta) {
+    const int blk = blockIdx.x * blockDim.x + threadIdx.x;
+    const int nblk = (n + kMetaRows - 1) / kMetaRows;
+    if (blk >= nblk) return;
+    int lo = 0x7fffffff, hi = -1, text = 0;
+    const int end = min(n, (blk + 1) * kMetaRows);
+    for (int i = blk * kMetaRows; i < end; ++i) {
+        const int id = ids[i];
+        if (id < 0) {
+            ++text;
+        } else {
+            lo = min(lo, id);
+            hi = max(hi, id);
+        }
+    }
+    int4 m;
+    m.x = lo;
+    m.y = hi;
+    m.z = text;
+    m.w = 0;
+    reinterpret_cast<int4*>(meta)[blk] = m;
+}
+
 }  // namespace
 
 hipError_t launch_fwd_pingpong(int D, const FwdParams& p, long long workgroups,
                                hipStream_t stream) {
     if (D == 64)
-        hipLaunchKernelGGL(attn_fwd_pp_kernel<64>, dim3((unsigned)workgroups), dim3(512), 0,
-                           stream, p);
+        hipLaunchKernelGGL((attn_fwd_pp_kernel<64, false>), dim3((unsigned)workgroups),
+                           dim3(512), 0, stream, p);
     else if (D == 128)
-        hipLaunchKernelGGL(attn_fwd_pp_kernel<128>, dim3((unsigned)workgroups), dim3(512), 0,
-                           stream, p);
+        hipLaunchKernelGGL((attn_fwd_pp_kernel<128, false>), dim3((unsigned)workgroups),
+                           dim3(512), 0, stream, p);
     else
         return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_fwd_block_causal(int D, const FwdParams& p, long long workgroups,
+                                   hipStream_t stream) {
+    if (!p.ids || !p.meta || p.splits != 1) return hipErrorInvalidValue;
+    if (D == 64)
+        hipLaunchKernelGGL((attn_fwd_pp_kernel<64, true>), dim3((unsigned)workgroups),
+                           dim3(512), 0, stream, p);
+    else if (D == 128)
+        hipLaunchKernelGGL((attn_fwd_pp_kernel<128, true>), dim3((unsigned)workgroups),
+                           dim3(512), 0, stream, p);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_bc_meta(const int* ids, int n, int* meta, hipStream_t stream) {
+    const int nblk = (n + kMetaRows - 1) / kMetaRows;
+    hipLaunchKernelGGL(attn_bc_meta_kernel, dim3((unsigned)((nblk + 255) / 256)), dim3(256), 0,
+                       stream, ids, n, meta);
     return hipGetLastError();
 }
 
