@@ -129,7 +129,8 @@ def cpu_baseline(w, seconds):
         rate = done * flop_per_row / el / 1e12
     return {"value": rate, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"{done} of {total_rows} query rows (first rows in [B,Nq,H] order) of "
-                      f"{w.name}, every visible key, FP64, {el:.1f} s"}
+                      f"{w.name}, every {'visible ' if w.kind == 'block_causal' else ''}key, "
+                      f"FP64, {el:.1f} s"}
 
 
 def bench_one(w, steps, warmup, torch, attn):
