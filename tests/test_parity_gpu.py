@@ -266,3 +266,36 @@ def test_workload_full_size(idx):
     sel = got if rows is None else got[rows]
     res = assert_accepted(sel, ref, w.name)
     say(f"workload {w.name}: {res}")
+
+
+# ---------------------------------------------------------------- HIP graph capture
+
+def test_graph_capture_replays_match_eager():
+    """Calls captured in a HIP graph (through torch's capture of the current stream)
+    replay to the eager bits, for a one-split call, a split-KV call (work space reserved
+    by an earlier uncaptured call) and a block-causal call. Eager work on the same
+    stream runs between replays."""
+    B, N, H, D = 1, 640, 4, 128
+    w = synth.small("dense", B, N, H, D, 1400, sigma_qk=2.0)
+    tq, tk, tv = (dev(t) for t in w.tensors())
+    ids = torch.from_numpy(ids_from([("text", 40), ("image", 500), ("text", 100)])).cuda()
+    calls = {
+        "dense": lambda out: attn.fwd_ex(tq, tk, tv, out=out, num_splits=1),
+        "split_kv": lambda out: attn.fwd_ex(tq, tk, tv, out=out, num_splits=4),
+        "block_causal": lambda out: attn.block_causal(tq, tk, tv, ids, out=out),
+    }
+    scratch = torch.ones(1 << 20, device="cuda")
+    for name, call in calls.items():
+        say(f"graph capture {name}")
+        eager = torch.empty_like(tq)
+        call(eager)  # also reserves any work space outside the capture
+        ref = host(eager).copy()
+        static_out = torch.zeros_like(tq)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            call(static_out)
+        for r in range(3):
+            static_out.zero_()
+            g.replay()
+            scratch.mul_(1.0001)  # unrelated eager work between replays
+            assert np.array_equal(host(static_out), ref), f"{name}: replay {r} differs"

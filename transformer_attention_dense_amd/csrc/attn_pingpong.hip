@@ -69,7 +69,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     static_assert(D == 64 || D == 128, "head dim");
     constexpr int NW = 8;
     constexpr int NT = NW * kWave;
-    constexpr int BN = 64;
+    constexpr int BN = 64;  // keys per tile (a multiple of 32)
     constexpr int NB = BN / 32;            // 32-key blocks per tile
     constexpr int KS = D / 16;             // MFMA k-steps over the head dim
     constexpr int DB = D / 32;             // 32-wide head-dim blocks of O^T
@@ -228,7 +228,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     };
 
     // G phase: MFMAs of S(t) (QK) and O += P(t-1) V(t-1) (PV), interleaved, with LDS
-    // operand fragments read three MFMAs ahead.
+    // operand fragments read PF MFMAs ahead.
     auto g_phase = [&](const char* kt, const char* vt, auto qk_c, auto pv_c) {
         constexpr bool QK = decltype(qk_c)::value;
         constexpr bool PV = decltype(pv_c)::value;
@@ -236,29 +236,28 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // fragment f: with both, even f = QK m = f/2, odd f = PV j = f/2
         auto is_qk = [](int f) { return QK && (!PV || (f % 2 == 0)); };
         auto idx = [](int f) { return (QK && PV) ? f / 2 : f; };
-        bf16x8 fr[4];
+        constexpr int PF = 3;  // fragments read ahead of their MFMA
+        bf16x8 fr[PF + 1];
         auto read_f = [&](auto fc) {
             constexpr int f = decltype(fc)::value;
             if constexpr (is_qk(f))
-                fr[f % 4] = read_k(kt, std::integral_constant<int, idx(f)>{});
+                fr[f % (PF + 1)] = read_k(kt, std::integral_constant<int, idx(f)>{});
             else
-                fr[f % 4] = read_v(vt, std::integral_constant<int, idx(f)>{});
+                fr[f % (PF + 1)] = read_v(vt, std::integral_constant<int, idx(f)>{});
         };
-        read_f(std::integral_constant<int, 0>{});
-        read_f(std::integral_constant<int, 1>{});
-        read_f(std::integral_constant<int, 2>{});
+        static_for<PF>([&](auto fc) { read_f(fc); });
         static_for<NF>([&](auto fc) {
             constexpr int f = decltype(fc)::value;
-            if constexpr (f + 3 < NF) read_f(std::integral_constant<int, f + 3>{});
+            if constexpr (f + PF < NF) read_f(std::integral_constant<int, f + PF>{});
             if constexpr (is_qk(f)) {
                 constexpr int m = idx(f);
                 s[m % NB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    fr[f % 4], qf[m / NB], (m < NB) ? f32x16{} : s[m % NB], 0, 0, 0);
+                    fr[f % (PF + 1)], qf[m / NB], (m < NB) ? f32x16{} : s[m % NB], 0, 0, 0);
             } else {
                 constexpr int j = idx(f);
                 constexpr int cc = j / DB, kb = cc / 2, tt = cc % 2, db = j % DB;
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[f % 4], pf[kb][tt], o[db], 0,
-                                                                0, 0);
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[f % (PF + 1)], pf[kb][tt],
+                                                                o[db], 0, 0, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
         });
@@ -276,15 +275,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         bool full = whole && t0 + BN - 1 <= q0;
         if (!full) {
             const int nblk = (p.Nq + kMetaRows - 1) / kMetaRows;
-            const int* km0 = p.meta + 4 * (t0 / kMetaRows);  // the tile's two row blocks
-            const int* km1 = p.meta + 4 * min(t0 / kMetaRows + 1, nblk - 1);
-            if (t0 > q0 + 31) {
-                const int kmin = min(km0[0], km1[0]), kmax = max(km0[1], km1[1]);
-                if (wq_max < 0 || kmax < wq_id || kmin > wq_max) return false;
+            // summaries of the tile's NB row blocks of 32 keys
+            int kmin = 0x7fffffff, kmax = -1;
+            bool uni = true;
+#pragma unroll
+            for (int kb = 0; kb < NB; ++kb) {
+                const int* km = p.meta + 4 * min(t0 / kMetaRows + kb, nblk - 1);
+                kmin = min(kmin, km[0]);
+                kmax = max(kmax, km[1]);
+                uni = uni && km[2] == 0 && km[0] == wq_id && km[1] == wq_id;
             }
-            if (whole && wq_uniform)
-                full = km0[2] == 0 && km1[2] == 0 && km0[0] == wq_id && km0[1] == wq_id &&
-                       km1[0] == wq_id && km1[1] == wq_id;
+            if (t0 > q0 + 31 && (wq_max < 0 || kmax < wq_id || kmin > wq_max)) return false;
+            if (whole && wq_uniform) full = uni;
         }
         if (full) return true;
         const int i = q0 + n;
@@ -333,15 +335,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     if (key >= kend) s[kb][r] = -INFINITY;
                 }
         }
-        // row maximum: four independent chains, then one exchange with lane ^ 32
+        // row maximum: four independent chains of EPC consecutive registers, then one
+        // exchange with lane ^ 32
+        constexpr int EPC = NB * 4;
+        auto sv = [&](int e) __attribute__((always_inline)) { return s[e / 16][e % 16]; };
         float m4[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) m4[k] = fmaxf(s[k / 2][8 * (k % 2)], s[k / 2][8 * (k % 2) + 1]);
+        for (int k = 0; k < 4; ++k) m4[k] = fmaxf(sv(k * EPC), sv(k * EPC + 1));
 #pragma unroll
         for (int k = 0; k < 4; ++k)
 #pragma unroll
-            for (int r = 2; r < 8; r += 2)
-                m4[k] = fmaxf(fmaxf(m4[k], s[k / 2][8 * (k % 2) + r]), s[k / 2][8 * (k % 2) + r + 1]);
+            for (int r = 2; r < EPC; r += 2)
+                m4[k] = fmaxf(fmaxf(m4[k], sv(k * EPC + r)), sv(k * EPC + r + 1));
         const float mx = wave_swap_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
         const bool need = (mx - m_ref) * c > kRescaleLog2;
         if (__builtin_amdgcn_ballot_w64(need) != 0) {
@@ -496,29 +501,30 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
 }
 
-// One thread per block of kMetaRows image ids: smallest and largest nonnegative id
-// and the number of negative (text) ids.
+// Summaries of the image ids, kMetaRows per block: thread i reads id i (coalesced);
+// each group of 32 lanes reduces its block with lane exchanges. Rows past n count as
+// neither text nor image.
 __global__ void attn_bc_meta_kernel(const int* ids, int n, int* meta) {
-    const int blk = blockIdx.x * blockDim.x + threadIdx.x;
-    const int nblk = (n + kMetaRows - 1) / kMetaRows;
-    if (blk >= nblk) return;
-    int lo = 0x7fffffff, hi = -1, text = 0;
-    const int end = min(n, (blk + 1) * kMetaRows);
-    for (int i = blk * kMetaRows; i < end; ++i) {
-        const int id = ids[i];
-        if (id < 0) {
-            ++text;
-        } else {
-            lo = min(lo, id);
-            hi = max(hi, id);
-        }
+    static_assert(kMetaRows == 32, "one half-wave per block of ids");
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    const int id = i < n ? ids[i] : -1;
+    int lo = (i < n && id >= 0) ? id : 0x7fffffff;
+    int hi = (i < n && id >= 0) ? id : -1;
+    int text = (i < n && id < 0) ? 1 : 0;
+#pragma unroll
+    for (int off = 16; off > 0; off >>= 1) {
+        lo = min(lo, __shfl_xor(lo, off, 32));
+        hi = max(hi, __shfl_xor(hi, off, 32));
+        text += __shfl_xor(text, off, 32);
     }
-    int4 m;
-    m.x = lo;
-    m.y = hi;
-    m.z = text;
-    m.w = 0;
-    reinterpret_cast<int4*>(meta)[blk] = m;
+    if ((i % kMetaRows) == 0 && i < n) {
+        int4 m;
+        m.x = lo;
+        m.y = hi;
+        m.z = text;
+        m.w = 0;
+        reinterpret_cast<int4*>(meta)[i / kMetaRows] = m;
+    }
 }
 
 }  // namespace
@@ -551,8 +557,7 @@ hipError_t launch_fwd_block_causal(int D, const FwdParams& p, long long workgrou
 }
 
 hipError_t launch_bc_meta(const int* ids, int n, int* meta, hipStream_t stream) {
-    const int nblk = (n + kMetaRows - 1) / kMetaRows;
-    hipLaunchKernelGGL(attn_bc_meta_kernel, dim3((unsigned)((nblk + 255) / 256)), dim3(256), 0,
+    hipLaunchKernelGGL(attn_bc_meta_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
                        stream, ids, n, meta);
     return hipGetLastError();
 }
