@@ -44,10 +44,11 @@ namespace {
 
 using namespace dev;
 
-template <int D, int NW, int BN>
+template <int D, int NW, int BN, int NSLOT>
 __global__ __launch_bounds__(NW* kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(FwdParams p) {
     static_assert(D == 64 || D == 128, "head dim");
-    static_assert(BN == 32 || BN == 64, "key tile");
+    static_assert(BN % 32 == 0 && BN <= 128, "key tile");
+    static_assert(NSLOT == 2 || NSLOT == 3, "LDS ring depth");
     constexpr int NB = BN / 32;            // 32-key blocks per tile
     constexpr int KS = D / 16;             // MFMA k-steps over the head dim
     constexpr int DB = D / 32;             // 32-wide head-dim blocks of O^T
@@ -59,7 +60,6 @@ __global__ __launch_bounds__(NW* kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
     static_assert(BN * CPR % NT == 0 && NT % CPR == 0, "loader");
 
     // Three K slots then three V slots, rows of 2*D bytes, chunks swizzled.
-    constexpr int NSLOT = 3;
     __shared__ __attribute__((aligned(1024))) char smem[2 * NSLOT * TILEB];
 
     int mb, bh, split;
@@ -326,10 +326,12 @@ __global__ __launch_bounds__(NW* kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
         });
     };
 
-    // Pipeline over the tiles of the range. Tile j of K and of V lives in slot j % 3.
-    // During tile t the loads of K(t+3) and V(t+2) are issued; at its end only the
-    // loads issued during tile t may still be in flight (K(t+2) and V(t+1) must have
-    // landed). One barrier per tile.
+    // Pipeline over the tiles of the range. Tile j of K and of V lives in slot
+    // j % NSLOT. Three slots: during tile t the loads of K(t+3) and V(t+2) are issued,
+    // and at its end only those may still be in flight (K(t+2) and V(t+1) must have
+    // landed). Two slots (half the LDS, so two workgroups fit on a CU with 64-key
+    // tiles at D = 128): K(t+2) and V(t+1) are issued and waited for within tile t.
+    // One barrier per tile.
     const int ntiles = (kend - kbeg + BN - 1) / BN;
     auto kslot = [&](int j) { return smem + (j % NSLOT) * TILEB; };
     auto vslot = [&](int j) { return smem + (NSLOT + j % NSLOT) * TILEB; };
@@ -337,13 +339,17 @@ __global__ __launch_bounds__(NW* kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
     issue_v(kbeg, 0);
     if (ntiles > 1) {
         issue_k(kbeg + BN, 1);
-        issue_v(kbeg + BN, 1);
+        if constexpr (NSLOT == 3) issue_v(kbeg + BN, 1);
     }
-    if (ntiles > 2) issue_k(kbeg + 2 * BN, 2);
+    if (NSLOT == 3 && ntiles > 2) issue_k(kbeg + 2 * BN, 2);
     barrier_vmcnt<0>();
     f32x16 sA[NB], sB[NB];
     if (active) qk_full(smem, sA);
-    barrier_vmcnt<2 * PER_T>();  // K slot 0 is refilled during the first tile
+    // K slot 0 is refilled during the first tile
+    if constexpr (NSLOT == 3)
+        barrier_vmcnt<2 * PER_T>();
+    else
+        barrier_vmcnt<0>();
 
     // One tile of the steady state. J = t mod 6 is a compile-time constant, so the
     // LDS slots (period 3) and the score buffers (period 2) fold into immediates.
@@ -352,16 +358,16 @@ __global__ __launch_bounds__(NW* kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
         f32x16(&sc)[NB] = (J % 2 == 0) ? sA : sB;
         f32x16(&sn)[NB] = (J % 2 == 0) ? sB : sA;
         const int t0 = kbeg + t * BN;
-        const bool more_k = t + 3 < ntiles;
-        const bool more_v = t + 2 < ntiles;
-        if (more_k) issue_k(t0 + 3 * BN, J % NSLOT);
-        if (more_v) issue_v(t0 + 2 * BN, (J + 2) % NSLOT);
+        const bool more_k = t + NSLOT < ntiles;
+        const bool more_v = t + NSLOT - 1 < ntiles;
+        if (more_k) issue_k(t0 + NSLOT * BN, J % NSLOT);
+        if (more_v) issue_v(t0 + (NSLOT - 1) * BN, (J + NSLOT - 1) % NSLOT);
         if (active)
             tile_pipelined(sc, sn, smem + ((J + 1) % NSLOT) * TILEB,
                            smem + (NSLOT + J % NSLOT) * TILEB);
-        if (more_k)
+        if (NSLOT == 3 && more_k)
             barrier_vmcnt<2 * PER_T>();
-        else if (more_v)
+        else if (NSLOT == 3 && more_v)
             barrier_vmcnt<PER_T>();
         else
             barrier_vmcnt<0>();
@@ -471,7 +477,9 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(CombineParams p) {
 
 template <int D, int NW>
 static hipError_t launch_fwd_t(const FwdParams& p, long long workgroups, hipStream_t stream) {
-    hipLaunchKernelGGL((attn_fwd_kernel<D, NW, key_tile(D)>), dim3((unsigned)workgroups),
+    // 64-key tiles; at D = 128 a two-slot ring keeps two workgroups per CU within LDS
+    constexpr int NSLOT = (D == 128) ? 2 : 3;
+    hipLaunchKernelGGL((attn_fwd_kernel<D, NW, kKeyTile, NSLOT>), dim3((unsigned)workgroups),
                        dim3(NW * kWave), 0, stream, p);
     return hipGetLastError();
 }

@@ -42,9 +42,7 @@ struct CombineParams {
     int splits;
 };
 
-// Keys per tile of the forward kernel: 32 at D = 128 (keeps two waves per SIMD within
-// the register budget), 64 at D = 64. Split ranges are multiples of 64 keys.
-constexpr int key_tile(int D) { return D == 128 ? 32 : 64; }
+// Keys per tile of the forward kernels; split ranges are multiples of it.
 constexpr int kKeyTile = 64;
 
 // waves 2 or 4: attn_fwd_kernel (attn_kernels.hip); waves 8: the ping-pong kernel
