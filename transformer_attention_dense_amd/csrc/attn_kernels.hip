@@ -477,9 +477,12 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(CombineParams p) {
 
 template <int D, int NW>
 static hipError_t launch_fwd_t(const FwdParams& p, long long workgroups, hipStream_t stream) {
-    // 64-key tiles; at D = 128 a two-slot ring keeps two workgroups per CU within LDS
-    constexpr int NSLOT = (D == 128) ? 2 : 3;
-    hipLaunchKernelGGL((attn_fwd_kernel<D, NW, kKeyTile, NSLOT>), dim3((unsigned)workgroups),
+    // Key tile and LDS ring depth: 64-key tiles in three slots at D = 64; at D = 128
+    // with 4 waves, 64-key tiles in two slots (64 KiB, two workgroups per CU); with 2
+    // waves, 32-key tiles in three slots (48 KiB, three workgroups per CU).
+    constexpr int BN = (D == 128 && NW == 2) ? 32 : kKeyTile;
+    constexpr int NSLOT = (D == 128 && NW == 4) ? 2 : 3;
+    hipLaunchKernelGGL((attn_fwd_kernel<D, NW, BN, NSLOT>), dim3((unsigned)workgroups),
                        dim3(NW * kWave), 0, stream, p);
     return hipGetLastError();
 }
