@@ -133,6 +133,32 @@ def cpu_baseline(w, seconds):
                       f"FP64, {el:.1f} s"}
 
 
+def graph_timing(torch, call, out):
+    """The pages' graph mode: 20 calls captured in one HIP graph (torch's capture of the
+    current stream), replayed 10 times; median microseconds per call. The output after
+    the replays is compared with the eager bits. Outside every timed region above;
+    None if capture is not possible here."""
+    try:
+        ref = out.clone()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(20):
+                call()
+        times = []
+        for _ in range(10):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            b.synchronize()
+            times.append(a.elapsed_time(b) * 1000.0 / 20)
+        return {"graph_call_us": round(statistics.median(times), 2),
+                "graph_output_matches_eager": bool(torch.equal(out, ref))}
+    except Exception as e:  # noqa: BLE001 - reported, the eager numbers stand
+        return {"graph_call_us": None, "graph_error": str(e)[:200]}
+
+
 def bench_one(w, steps, warmup, torch, attn):
     ts = w.tensors()
     if w.kind == "block_causal":  # Q, K, V bits and the int32 image ids
@@ -170,8 +196,10 @@ def bench_one(w, steps, warmup, torch, attn):
                 "workspace_bytes": 16 * -(-w.Nq // 32), "block_causal": True}
     else:
         plan = attn.attn_plan(w.B, w.Nq, w.keys, w.H, w.D)
+    finite = bool(torch.isfinite(out.float()).all())
+    graph = graph_timing(torch, call, out)
     return {"wall_s": wall, "event_ms": ev_ms, "median_call_us": statistics.median(samples),
-            "plan": plan, "finite": bool(torch.isfinite(out.float()).all())}
+            "plan": plan, "finite": finite, "graph": graph}
 
 
 def kernel_name(D, plan):
@@ -209,6 +237,7 @@ def record(w, r, steps, warmup, cpu):
                    "workgroups": r["plan"]["workgroups"]},
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "median_call_us": round(r["median_call_us"], 2),
+        **r["graph"],
         "roofline": {
             "bound": "mfma",
             "achieved": round(achieved, 2),
