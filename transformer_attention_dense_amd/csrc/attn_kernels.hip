@@ -344,7 +344,7 @@ __global__ __launch_bounds__(NW* kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
     if (NSLOT == 3 && ntiles > 2) issue_k(kbeg + 2 * BN, 2);
     barrier_vmcnt<0>();
     f32x16 sA[NB], sB[NB];
-    if (active) qk_full(smem, sA);
+    if (active) qk_full(kslot(0), sA);
     // K slot 0 is refilled during the first tile
     if constexpr (NSLOT == 3)
         barrier_vmcnt<2 * PER_T>();
@@ -363,8 +363,7 @@ __global__ __launch_bounds__(NW* kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
         if (more_k) issue_k(t0 + NSLOT * BN, J % NSLOT);
         if (more_v) issue_v(t0 + (NSLOT - 1) * BN, (J + NSLOT - 1) % NSLOT);
         if (active)
-            tile_pipelined(sc, sn, smem + ((J + 1) % NSLOT) * TILEB,
-                           smem + (NSLOT + J % NSLOT) * TILEB);
+            tile_pipelined(sc, sn, kslot(J + 1), vslot(J));
         if (NSLOT == 3 && more_k)
             barrier_vmcnt<2 * PER_T>();
         else if (NSLOT == 3 && more_v)
