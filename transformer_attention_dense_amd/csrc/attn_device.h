@@ -101,6 +101,40 @@ __device__ __forceinline__ void load16_to_lds(const uint16_t* src, char* dst) {
 #pragma clang diagnostic pop
 }
 
+// A 64-bit value that is the same for the whole wave, moved to scalar registers. The
+// halves go through readfirstlane, which returns int: each is converted to unsigned
+// before widening, so the low half is zero-extended, never sign-extended.
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t a) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((unsigned)a);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
+    return ((uint64_t)hi << 32) | (uint64_t)lo;
+}
+
+// The same copy with a wave-uniform base address and a per-lane 32-bit byte offset:
+// the load adds them itself (scalar-base form), so issuing it takes no vector
+// instructions. base must be the same for the whole wave.
+__device__ __forceinline__ void load16_to_lds_sbase(const void* base, unsigned voff, char* dst) {
+    const unsigned lds = __builtin_amdgcn_readfirstlane(
+        (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)dst);
+    const uint64_t sb = uniform_u64((uint64_t)(uintptr_t)base);
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+    __asm__ volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %1"
+        :
+        : "v"(voff), "s"(sb), "s"(lds)
+        : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
+// A pointer that is the same for the whole wave, kept in scalar registers.
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* ptr) {
+    return reinterpret_cast<T*>((uintptr_t)uniform_u64((uint64_t)(uintptr_t)ptr));
+}
+
 // XOR swizzle of the 16-byte chunks of LDS row r (CPR chunks per row, period 16
 // rows). Chunk c of row r is stored at chunk position c ^ lds_swizzle(r). Chosen so
 // that (a) the 16 lanes of a K operand read (16 consecutive rows, one logical chunk)

@@ -82,10 +82,12 @@ __global__ __launch_bounds__(NW* kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
     const bool active = q0 < p.Nq;
 
     // Per-(batch, head) bases of the two key segments (element offsets of row 0).
-    const uint16_t* kseg0 = p.k0 + ((long)b * n0 * HD + (long)h * D);
-    const uint16_t* vseg0 = p.v0 + ((long)b * n0 * HD + (long)h * D);
-    const uint16_t* kseg1 = p.k1 ? p.k1 + ((long)b * p.n1 * HD + (long)h * D) : kseg0;
-    const uint16_t* vseg1 = p.v1 ? p.v1 + ((long)b * p.n1 * HD + (long)h * D) : vseg0;
+    const uint16_t* kseg0 = uniform_ptr(p.k0 + ((long)b * n0 * HD + (long)h * D));
+    const uint16_t* vseg0 = uniform_ptr(p.v0 + ((long)b * n0 * HD + (long)h * D));
+    const uint16_t* kseg1 =
+        uniform_ptr(p.k1 ? p.k1 + ((long)b * p.n1 * HD + (long)h * D) : kseg0);
+    const uint16_t* vseg1 =
+        uniform_ptr(p.v1 ? p.v1 + ((long)b * p.n1 * HD + (long)h * D) : vseg0);
 
     // Q^T fragments (B operand), one per 16-dim k-step: lane holds query n, dims
     // 16*ks + 8g .. +7.
@@ -122,12 +124,9 @@ __global__ __launch_bounds__(NW* kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
             const long rowoff = (t0 < n0) ? (long)t0 * HD : (long)(t0 - n0) * HD;
             const uint16_t* base = ((t0 < n0) ? seg0 : seg1) + rowoff;
 #pragma unroll
-            for (int i = 0; i < PER_T; ++i) {
-                const uint16_t* rb = base + (long)(i / NPAT) * NPAT * RSTEP * HD;  // uniform
-                load16_to_lds(reinterpret_cast<const uint16_t*>(
-                                  reinterpret_cast<const char*>(rb) + (unsigned)(2 * ld_off[i % NPAT])),
-                              dst + i * NT * 16);
-            }
+            for (int i = 0; i < PER_T; ++i)  // uniform base, per-lane offset
+                load16_to_lds_sbase(base + (long)(i / NPAT) * NPAT * RSTEP * HD,
+                                    2u * ld_off[i % NPAT], dst + i * NT * 16);
         } else {
             // ragged or segment-straddling tile: clamp rows into [t0, kend) and pick
             // the segment per row
