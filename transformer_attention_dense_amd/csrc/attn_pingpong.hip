@@ -78,11 +78,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     constexpr int TILEB = BN * ROWB;       // bytes per K or V tile
     constexpr int PER_T = BN * CPR / NT;   // 16-byte copies per thread per tensor per tile
     constexpr int RSTEP = NT / CPR;        // rows per copy round
+    constexpr int NTG = NT / 2;            // threads of one wave group
+    constexpr int PER_G = BN * CPR / NTG;  // copies per thread of a group copying a tile
+    constexpr int RSTEP_G = NTG / CPR;     // rows per copy round of a group
     constexpr int NSLOT = 3;
     constexpr int NQ = KS * NB;            // QK^T MFMAs per tile
     constexpr int NP = 2 * NB * DB;        // PV MFMAs per tile
     constexpr int NPAIR = NB * 8;          // exp pairs per lane per tile
     static_assert(BN * CPR % NT == 0 && RSTEP % 16 == 0, "loader pattern");
+    static_assert(BN * CPR % NTG == 0 && RSTEP_G % 16 == 0, "group loader pattern");
 
     __shared__ __attribute__((aligned(1024))) char smem[2 * NSLOT * TILEB];
 
@@ -171,10 +175,40 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             }
         }
     };
+    // Group loader: the same pattern over the 256 threads of this wave's group, so one
+    // group copies a whole tile (the group in its softmax phase issues the copies; the
+    // other one goes straight to its MFMAs).
+    const int tidg = tid & (NTG - 1);
+    const int ldg_row0 = tidg / CPR;
+    const int ldg_off = ldg_row0 * HD + ((tidg % CPR) ^ lds_swizzle<CPR>(ldg_row0)) * 8;
+    auto issue_g = [&](const uint16_t* seg0, const uint16_t* seg1, int t0, char* slot) {
+        char* const dst = slot + (wave & 3) * kWave * 16;
+        const bool whole = (t0 + BN <= kend) && (t0 + BN <= n0 || t0 >= n0);
+        if (whole) {
+            const long rowoff = (t0 < n0) ? (long)t0 * HD : (long)(t0 - n0) * HD;
+            const uint16_t* base = ((t0 < n0) ? seg0 : seg1) + rowoff;
+#pragma unroll
+            for (int i = 0; i < PER_G; ++i)  // uniform base, per-lane offset
+                load16_to_lds_sbase(base + (long)i * RSTEP_G * HD, 2u * ldg_off,
+                                    dst + i * NTG * 16);
+        } else {
+#pragma unroll
+            for (int i = 0; i < PER_G; ++i) {
+                const int r = ldg_row0 + i * RSTEP_G;
+                const int key = min(t0 + r, kend - 1);
+                const int co = ldg_off - ldg_row0 * HD;
+                const uint16_t* src =
+                    key < n0 ? seg0 + (long)key * HD : seg1 + (long)(key - n0) * HD;
+                load16_to_lds(src + co, dst + i * NTG * 16);
+            }
+        }
+    };
     auto kslot = [&](int j) { return smem + j * TILEB; };
     auto vslot = [&](int j) { return smem + (NSLOT + j) * TILEB; };
     auto issue_k = [&](int t0, int slot) { issue(kseg0, kseg1, t0, kslot(slot)); };
     auto issue_v = [&](int t0, int slot) { issue(vseg0, vseg1, t0, vslot(slot)); };
+    auto issue_kg = [&](int t0, int slot) { issue_g(kseg0, kseg1, t0, kslot(slot)); };
+    auto issue_vg = [&](int t0, int slot) { issue_g(vseg0, vseg1, t0, vslot(slot)); };
 
     // Per-lane LDS byte offsets: K operand reads per k-step, V transpose reads per
     // head-dim block and 8-key half.
@@ -387,12 +421,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // then G(u).
     auto run = [&](auto grp_c) {
         constexpr int GRP = decltype(grp_c)::value;
-        // phase 0 (tile 0): copies for K(2), V(1); group 0 computes S(0)
-        if (T > 2) issue_k(kbeg + 2 * BN, 2);
-        if (T > 1) issue_v(kbeg + BN, 1);
+        // phase 0 (tile 0): group 1 copies K(2); group 0 computes S(0)
+        if (GRP == 1 && T > 2) issue_kg(kbeg + 2 * BN, 2);
         if (GRP == 0 && active) g_phase(kslot(0), vslot(0), TRUE_{}, FALSE_{});
         barrier_vmcnt<63>();
-        // phase 1: group 0 softmax of tile 0, group 1 computes S(0)
+        // phase 1: group 0 copies V(1) and runs the softmax of tile 0, group 1
+        // computes S(0)
+        if (GRP == 0 && T > 1) issue_vg(kbeg + BN, 1);
         if (active) {
             if (GRP == 0)
                 s_phase(kbeg);
@@ -403,14 +438,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         auto tile = [&](int u, auto jc) {
             constexpr int J = decltype(jc)::value;
             const int t0 = kbeg + u * BN;
-            // K(u) and V(u-1) were copied two phases ago; the copies of the last
-            // phase pair (K(u+1) if any, V(u)) may stay in flight.
-            if (u + 1 < T)
-                barrier_vmcnt<2 * PER_T>();
-            else
-                barrier_vmcnt<PER_T>();
-            if (u + 2 < T) issue_k(t0 + 2 * BN, (J + 2) % NSLOT);
-            if (u + 1 < T) issue_v(t0 + BN, (J + 1) % NSLOT);
+            // This tile reads K(u) and V(u-1). Group 1 copies the K tiles (first phase
+            // of a tile), group 0 the V tiles (second phase); each waits for its own:
+            // group 1 may keep K(u+1) in flight, group 0 V(u).
+            if (GRP == 1) {
+                if (u + 1 < T)
+                    barrier_vmcnt<PER_G>();
+                else
+                    barrier_vmcnt<0>();
+            } else {
+                barrier_vmcnt<PER_G>();
+            }
+            if (GRP == 1 && u + 2 < T) issue_kg(t0 + 2 * BN, (J + 2) % NSLOT);
             if (active) {
                 if (GRP == 0)
                     g_phase(kslot(J), vslot((J + 2) % NSLOT), TRUE_{}, TRUE_{});
@@ -418,6 +457,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     s_phase(t0 - BN);
             }
             barrier_vmcnt<63>();
+            if (GRP == 0 && u + 1 < T) issue_vg(t0 + BN, (J + 1) % NSLOT);
             if (active) {
                 if (GRP == 0)
                     s_phase(t0);
