@@ -51,6 +51,8 @@ def _lib():
                                          ctypes.c_double]
         lib.oracle_block_causal_rows.restype = ctypes.c_int
         lib.oracle_block_causal_rows.argtypes = [p, p, p, p, L, L, L, L, p, L, p, p, p]
+        lib.oracle_na3d_rows.restype = ctypes.c_int
+        lib.oracle_na3d_rows.argtypes = [p, p, p] + [L] * 9 + [p, L, p]
         lib.oracle_num_threads.restype = ctypes.c_int
         _LIB = lib
     return _LIB
@@ -178,3 +180,41 @@ def block_causal_attention(q, k, v, image_ids):
     """Block-causal attention (no prefix), full output [B, N, H, D] in FP64."""
     B, N, H, D = q.shape
     return block_causal_rows(q, k, v, image_ids).reshape(B, N, H, D)
+
+
+def _bits6(a, name):
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint16 or a.ndim != 6:
+        raise TypeError(f"{name}: expected uint16 BF16 bits of rank 6, got {a.dtype} {a.shape}")
+    return a
+
+
+def na3d_rows(q, k, v, kernel, rows=None):
+    """FP64 3-D neighborhood attention for selected query rows.
+
+    q, k, v: [B, T, Y, X, H, D] bits; kernel = (kt, ky, kx), odd, each at most its
+    axis. rows: flat indices ((((b*T + t)*Y + y)*X + x)*H + h), or None for every row.
+    Returns out [rows, D].
+    """
+    q, k, v = _bits6(q, "q"), _bits6(k, "k"), _bits6(v, "v")
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError(f"k {k.shape} / v {v.shape} must match q {q.shape}")
+    B, T, Y, X, H, D = q.shape
+    kt, ky, kx = (int(x) for x in kernel)
+    if rows is None:
+        nrows = B * T * Y * X * H
+        rows_arr = None
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        nrows = rows_arr.size
+    out = np.empty((nrows, D), dtype=np.float64)
+    rc = _lib().oracle_na3d_rows(_ptr(q), _ptr(k), _ptr(v), B, T, Y, X, H, D, kt, ky, kx,
+                                 _ptr(rows_arr), nrows, _ptr(out))
+    if rc != 0:
+        raise RuntimeError(f"oracle_na3d_rows failed with code {rc}")
+    return out
+
+
+def na3d_attention(q, k, v, kernel):
+    """3-D neighborhood attention, full output [B, T, Y, X, H, D] in FP64."""
+    return na3d_rows(q, k, v, kernel).reshape(q.shape)

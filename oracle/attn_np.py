@@ -62,3 +62,37 @@ def block_causal_visibility(image_ids) -> np.ndarray:
 
 def block_causal_attention(q, k, v, image_ids):
     return attention(q, k, v, allowed=block_causal_visibility(image_ids))
+
+
+def na_window_search(L: int, k: int) -> np.ndarray:
+    """[L, L] boolean: position i sees j on an axis of length L with an odd window k.
+    Among all windows of k consecutive positions inside [0, L) that contain i, the one
+    whose centre is nearest to i (a search over the windows, independent of the start
+    formula of the C oracle)."""
+    vis = np.zeros((L, L), dtype=bool)
+    for i in range(L):
+        best = None
+        for s in range(0, L - k + 1):
+            if s <= i < s + k:
+                dist = abs(s + k // 2 - i)
+                if best is None or dist < best[0]:
+                    best = (dist, s)
+        vis[i, best[1]:best[1] + k] = True
+    return vis
+
+
+def na3d_visibility(T: int, Y: int, X: int, kernel) -> np.ndarray:
+    """[T*Y*X, T*Y*X] boolean visibility of 3-D neighborhood attention: the product of
+    the per-axis windows, positions flattened as (t*Y + y)*X + x."""
+    kt, ky, kx = kernel
+    vt, vy, vx = na_window_search(T, kt), na_window_search(Y, ky), na_window_search(X, kx)
+    return (vt[:, None, None, :, None, None] & vy[None, :, None, None, :, None] &
+            vx[None, None, :, None, None, :]).reshape(T * Y * X, T * Y * X)
+
+
+def na3d_attention(q, k, v, kernel):
+    """[B, T, Y, X, H, D] -> FP64 [B, T, Y, X, H, D]; scores are plain dot products."""
+    B, T, Y, X, H, D = q.shape
+    flat = lambda a: a.reshape(B, T * Y * X, H, D)
+    o = attention(flat(q), flat(k), flat(v), scale=1.0, allowed=na3d_visibility(T, Y, X, kernel))
+    return o.reshape(B, T, Y, X, H, D)

@@ -222,6 +222,109 @@ int oracle_block_causal_rows(const uint16_t* q, const uint16_t* k, const uint16_
     return fail ? -fail : 0;
 }
 
+/* Window of odd size k around position i on an axis of length L (k <= L): the k
+ * consecutive positions centred on i, moved inside [0, L) at the ends, so every query
+ * has exactly k neighbours on the axis. This is the neighborhood the pages' 3-D
+ * neighborhood attention delegates to (natten.functional.na3d with its defaults); the
+ * pages do not spell it out, and this is NATTEN's published definition. */
+static void na_window(long i, long k, long L, long* lo, long* hi) {
+    long s = i - k / 2;
+    if (s > L - k) s = L - k;
+    if (s < 0) s = 0;
+    *lo = s;
+    *hi = s + k;
+}
+
+/*
+ * 3-D neighborhood attention (page "Audit SGLang interfaces and refresh validated
+ * kernel solutions", definitions/neighborhood_attention/
+ * neighborhood_attention_3d_h{4,8,16,32}_d64_kt*_ky*_kx*, called as
+ * natten.functional.na3d(query, key, value, kernel_size, scale=1.0); the model's scale
+ * is already in Q). q, k, v and out rows use the layout [B, T, Y, X, H, D]. Query
+ * (b, t, y, x, h) attends to the kt*ky*kx keys (b, t', y', x', h) with t' in the
+ * window of t on the T axis, y' in that of y, x' in that of x (na_window); its score
+ * with a key is the plain dot product (scale 1).
+ *
+ * rows: flat query indices ((((b*T + t)*Y + y)*X + x)*H + h), or NULL for all.
+ * Returns 0; -1 bad arguments (null, size < 1, even window or window longer than its
+ * axis); -2 row index out of range; -3 allocation failure.
+ */
+int oracle_na3d_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, long B, long T,
+                     long Y, long X, long H, long D, long kt, long ky, long kx,
+                     const long* rows, long nrows, double* out) {
+    if (!q || !k || !v || !out || B < 1 || T < 1 || Y < 1 || X < 1 || H < 1 || D < 1) return -1;
+    if (kt < 1 || ky < 1 || kx < 1 || kt % 2 == 0 || ky % 2 == 0 || kx % 2 == 0) return -1;
+    if (kt > T || ky > Y || kx > X) return -1;
+    const long total = B * T * Y * X * H;
+    if (!rows) nrows = total;
+    const long nkeys = kt * ky * kx;
+    int fail = 0;
+
+#pragma omp parallel
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)nkeys);
+        long* kidx = (long*)malloc(sizeof(long) * (size_t)nkeys);
+        double* qd = (double*)malloc(sizeof(double) * (size_t)D);
+        if (!s || !kidx || !qd) {
+#pragma omp atomic write
+            fail = 3;
+        } else {
+#pragma omp for schedule(dynamic, 16)
+            for (long r_i = 0; r_i < nrows; ++r_i) {
+                const long r = rows ? rows[r_i] : r_i;
+                if (r < 0 || r >= total) {
+#pragma omp atomic write
+                    fail = 2;
+                    continue;
+                }
+                const long h = r % H;
+                const long pos = r / H;
+                const long x = pos % X;
+                const long y = (pos / X) % Y;
+                const long t = (pos / (X * Y)) % T;
+                const long b = pos / (X * Y * T);
+                const uint16_t* qr = q + (pos * H + h) * D;
+                for (long d = 0; d < D; ++d) qd[d] = bf16_to_f64(qr[d]);
+
+                long t0, t1, y0, y1, x0, x1;
+                na_window(t, kt, T, &t0, &t1);
+                na_window(y, ky, Y, &y0, &y1);
+                na_window(x, kx, X, &x0, &x1);
+                long n = 0;
+                double mx = -INFINITY;
+                for (long tt = t0; tt < t1; ++tt)
+                    for (long yy = y0; yy < y1; ++yy)
+                        for (long xx = x0; xx < x1; ++xx) {
+                            const long kp = ((b * T + tt) * Y + yy) * X + xx;
+                            const uint16_t* kr = k + (kp * H + h) * D;
+                            double dot = 0.0;
+                            for (long d = 0; d < D; ++d) dot += qd[d] * bf16_to_f64(kr[d]);
+                            kidx[n] = kp;
+                            s[n] = dot;
+                            if (dot > mx) mx = dot;
+                            ++n;
+                        }
+                double l = 0.0;
+                for (long j = 0; j < n; ++j) {
+                    s[j] = exp(s[j] - mx);
+                    l += s[j];
+                }
+                double* o = out + r_i * D;
+                for (long d = 0; d < D; ++d) o[d] = 0.0;
+                for (long j = 0; j < n; ++j) {
+                    const double pj = s[j] / l;
+                    const uint16_t* vr = v + (kidx[j] * H + h) * D;
+                    for (long d = 0; d < D; ++d) o[d] += pj * bf16_to_f64(vr[d]);
+                }
+            }
+        }
+        free(s);
+        free(kidx);
+        free(qd);
+    }
+    return fail ? -fail : 0;
+}
+
 /* Number of OpenMP threads the oracle will use (1 when built without OpenMP). */
 int oracle_num_threads(void) {
 #ifdef _OPENMP

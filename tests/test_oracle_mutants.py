@@ -45,6 +45,14 @@ MUTANTS = {
                                  "const int same_image = ids[i] == ids[j];"),
     "bc_image_sees_everything": ("const int same_image = ids[i] >= 0 && ids[i] == ids[j];",
                                  "const int same_image = ids[i] >= 0;"),
+    "na_window_not_moved_inside": ("    if (s > L - k) s = L - k;\n    if (s < 0) s = 0;\n    *lo = s;\n    *hi = s + k;",
+                                   "    *lo = s < 0 ? 0 : s;\n    *hi = (i + k / 2 + 1 < L) ? i + k / 2 + 1 : L;"),
+    "na_window_off_centre": ("    long s = i - k / 2;", "    long s = i - k / 2 + 1;"),
+    "na_axes_y_x_swapped": ("                na_window(y, ky, Y, &y0, &y1);\n                na_window(x, kx, X, &x0, &x1);",
+                            "                na_window(y, kx, X, &y0, &y1);\n                na_window(x, ky, Y, &x0, &x1);"),
+    "na_scaled_by_head_dim": ("                            s[n] = dot;", "                            s[n] = dot * pow((double)D, -0.5);"),
+    "na_values_of_first_key": ("                    const uint16_t* vr = v + (kidx[j] * H + h) * D;",
+                               "                    const uint16_t* vr = v + (kidx[0] * H + h) * D;"),
     "bc_key_id_index": ("const int same_image = ids[i] >= 0 && ids[i] == ids[j];",
                         "const int same_image = ids[i] >= 0 && ids[i] == ids[j > 0 ? j - 1 : 0];"),
 }
@@ -63,7 +71,8 @@ def _run_pins(lib):
     env = dict(os.environ, ORACLE_LIB=lib, OMP_NUM_THREADS="2")
     return subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
                            os.path.join(ROOT, "tests", "test_oracle.py"),
-                           os.path.join(ROOT, "tests", "test_oracle_block_causal.py")],
+                           os.path.join(ROOT, "tests", "test_oracle_block_causal.py"),
+                           os.path.join(ROOT, "tests", "test_oracle_na3d.py")],
                           cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
 
 
