@@ -40,6 +40,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
 DEFAULT_WORKLOAD = "dense_b1_n4096_h32_d128"
 KERNEL_SOURCES = ["transformer_attention_dense_amd/csrc/attn_kernels.hip",
                   "transformer_attention_dense_amd/csrc/attn_pingpong.hip",
+                  "transformer_attention_dense_amd/csrc/attn_na3d.hip",
                   "transformer_attention_dense_amd/csrc/attn_device.h",
                   "transformer_attention_dense_amd/csrc/attn_api.hip",
                   "transformer_attention_dense_amd/csrc/attn_launch.h"]
@@ -74,6 +75,9 @@ def to_device(bits, torch):
 
 
 def make_call(w, dts, attn):
+    if w.kind == "na3d":
+        out = attn.na3d(*dts, w.kernel)
+        return out, (lambda: attn.na3d(*dts, w.kernel, out=out))
     if w.kind == "block_causal":
         out = attn.block_causal(*dts)
         return out, (lambda: attn.block_causal(*dts, out=out))
@@ -114,6 +118,8 @@ def cpu_baseline(w, seconds):
         rows = np.arange(done, min(done + chunk, total_rows), dtype=np.int64)
         if w.kind == "block_causal":
             oracle.block_causal_rows(ts[0], ts[1], ts[2], ts[3], rows=rows)
+        elif w.kind == "na3d":
+            oracle.na3d_rows(ts[0], ts[1], ts[2], w.kernel, rows=rows)
         else:
             oracle.attention_rows(ts[0], ts[1], ts[2], *ts[3:5], rows=rows)
         done += rows.size
@@ -194,6 +200,10 @@ def bench_one(w, steps, warmup, torch, attn):
     if w.kind == "block_causal":  # always one split of the 8-wave kernel
         plan = {"splits": 1, "waves": 8, "workgroups": -(-w.Nq // 256) * w.B * w.H,
                 "workspace_bytes": 16 * -(-w.Nq // 32), "block_causal": True}
+    elif w.kind == "na3d":  # one wave per 32-query strip and head, four heads per workgroup
+        T, Y, X = w.grid
+        plan = {"splits": 1, "waves": 4, "workgroups": w.B * T * Y * -(-X // 32) * -(-w.H // 4),
+                "workspace_bytes": 0, "na3d": True}
     else:
         plan = attn.attn_plan(w.B, w.Nq, w.keys, w.H, w.D)
     finite = bool(torch.isfinite(out.float()).all())
@@ -207,6 +217,8 @@ def kernel_name(D, plan):
     waves = plan["waves"]
     if plan.get("block_causal"):
         return f"attn_bc_meta_kernel + attn_fwd_pp_kernel<{D}, true>"
+    if plan.get("na3d"):
+        return "attn_na3d_kernel"
     main = (f"attn_fwd_pp_kernel<{D}, false>" if waves == 8 else
             f"attn_fwd_kernel<{D}, {waves}, {32 if D == 128 else 64}>")
     return main if plan["splits"] == 1 else main + f" + attn_combine_kernel<{D}>"
@@ -258,6 +270,8 @@ def record(w, r, steps, warmup, cpu):
                                 "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                 "frac": round(rec["roofline"]["hbm_gbs_algorithmic"]
                                               / PEAK_HBM_GBS, 4)})
+    if w.kind == "na3d":
+        rec["config"].update({"grid": list(w.grid), "kernel": list(w.kernel)})
     if cpu is not None:
         rec["cpu_baseline"] = cpu
     return rec

@@ -95,6 +95,25 @@ int attn_block_causal(const void* q, const void* k, const void* v, const int* im
                       void* out, int B, int N, int H, int D, void* stream);
 
 /*
+ * 3-D neighborhood attention (page "Audit SGLang interfaces and refresh validated kernel
+ * solutions", definitions/neighborhood_attention/neighborhood_attention_3d_*: the call
+ * natten.functional.na3d(q, k, v, kernel_size=(kt, ky, kx), scale=1.0); the model's
+ * scale is already in Q).
+ *   q, k, v, out: [B, T, Y, X, H, D] BF16, contiguous, device memory, D = 64.
+ *   Query (b, t, y, x, h) attends to the keys (b, t', y', x', h) with t' in the window of
+ *   t on the T axis (odd size kt, centred on t and moved inside [0, T) at the ends:
+ *   start = max(0, min(t - kt/2, T - kt))), likewise y' on Y with ky and x' on X with
+ *   kx: exactly kt*ky*kx keys each. Scores are plain dot products (scale 1); softmax in
+ *   FP32, output rounded to BF16. The neighborhood is NATTEN's published one; the pages
+ *   name na3d without defining it.
+ * Errors: ATTN_ERR_SHAPE for a size < 1 or a window that is even or longer than its
+ * axis; ATTN_ERR_UNSUPPORTED for D != 64 or kx > 33; ATTN_ERR_OVERFLOW, ATTN_ERR_ALIGN,
+ * ATTN_ERR_ALIAS as for the other calls. No work space.
+ */
+int attn_na3d(const void* q, const void* k, const void* v, void* out, int B, int T, int Y,
+              int X, int H, int D, int kt, int ky, int kx, void* stream);
+
+/*
  * General form behind the dense, prefix and cross calls, with explicit launch options.
  * The keys are segment 0 (k0/v0, n0 rows) followed by segment 1 (k1/v1, n1 rows);
  * n0 + n1 >= 1, and a segment with zero rows may have NULL pointers.

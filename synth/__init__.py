@@ -81,6 +81,8 @@ class Workload:
     kind "prefix": Q [B,Nq,H,D], K/V_prefix [B,Np,H,D], K/V_current [B,Nq,H,D].
     kind "block_causal": Q, K_current, V_current [B,Nq,H,D] and image_ids [Nq] from
     ``segments`` (a list of ("text" | "image", length) pairs summing to Nq).
+    kind "na3d": Q, K, V [B,T,Y,X,H,D] (``grid`` = (T, Y, X)), 3-D neighborhood attention
+    with window ``kernel``; every query sees kt*ky*kx keys.
     """
     name: str
     kind: str
@@ -95,10 +97,17 @@ class Workload:
     outliers: int = 0     # channels per head scaled by outlier_factor in Q and K
     outlier_factor: float = 8.0
     segments: Tuple[Tuple[str, int], ...] = ()
+    grid: Tuple[int, int, int] = ()     # na3d: (T, Y, X); Nq = T*Y*X positions
+    kernel: Tuple[int, int, int] = ()   # na3d: (kt, ky, kx) window sizes
     description: str = ""
     extra: Dict = field(default_factory=dict)
 
     def __post_init__(self):
+        if self.kind == "na3d":
+            T, Y, X = self.grid
+            self.Nq = T * Y * X
+            if any(k % 2 == 0 or k > L for k, L in zip(self.kernel, self.grid)):
+                raise ValueError(f"{self.name}: windows must be odd and fit their axes")
         if self.kind in ("dense", "block_causal") and self.Nk == 0:
             self.Nk = self.Nq
         if self.kind == "block_causal":
@@ -144,6 +153,10 @@ class Workload:
 
     @property
     def keys(self) -> int:
+        """Keys per query row."""
+        if self.kind == "na3d":
+            kt, ky, kx = self.kernel
+            return kt * ky * kx
         return self.Np + self.Nq if self.kind == "prefix" else self.Nk
 
     @property
@@ -164,6 +177,8 @@ class Workload:
     def algorithmic_bytes(self) -> int:
         """Every input read once and the output written once, 2 bytes per element."""
         q = self.B * self.Nq * self.H * self.D
+        if self.kind == "na3d":  # Q, K, V and O all cover the whole volume
+            return 2 * 4 * q
         kv = 2 * self.B * self.keys * self.H * self.D
         ids = 4 * self.Nq if self.kind == "block_causal" else 0  # int32 image ids
         return 2 * (q + kv + q) + ids
@@ -175,6 +190,10 @@ class Workload:
         """Arrays in call order: BF16 bits (Q, K, V) or (Q, Kp, Vp, Kc, Vc); block-causal
         (Q, K_current, V_current, image_ids)."""
         B, Nq, H, D = self.B, self.Nq, self.H, self.D
+        if self.kind == "na3d":  # Q carries the model's scale: sigma_qk
+            shape = (B,) + tuple(self.grid) + (H, D)
+            return (normal_bf16(shape, self.seed(0), self.sigma_qk),
+                    normal_bf16(shape, self.seed(1), 1.0), normal_bf16(shape, self.seed(2), 1.0))
         if self.kind == "block_causal":
             return tuple(normal_bf16((B, Nq, H, D), self.seed(t), self.sigma_qk if t < 2 else 1.0)
                          for t in range(3)) + (self.image_ids(),)
@@ -232,6 +251,18 @@ WORKLOADS.append(
              description="Block-causal attention without prefix, B=1 N=4096 H=32 D=128: "
                          "text 128, image 1920, text 64, image 1920, text 64; N(0,1), "
                          "scale 1/sqrt(128)"))
+
+# 3-D neighborhood attention (the pages' four na3d definitions, D = 64, scale 1 with the
+# model's scale folded into Q; the pages print window sizes and head counts but no volume
+# shapes): decoder-like volumes, Q ~ N(0, 1/64), K, V ~ N(0, 1); indices 7..10.
+for _i, (_g, _h, _k) in enumerate((((8, 64, 64), 16, (3, 7, 7)), ((8, 32, 32), 32, (3, 7, 7)),
+                                   ((16, 32, 32), 4, (11, 11, 11)), ((8, 64, 64), 8, (3, 5, 5)))):
+    WORKLOADS.append(Workload(
+        f"na3d_b1_t{_g[0]}_y{_g[1]}_x{_g[2]}_h{_h}_d64_k{_k[0]}x{_k[1]}x{_k[2]}", "na3d", 1, 0,
+        _h, 64, 7 + _i, grid=_g, kernel=_k, sigma_qk=0.125,
+        description=f"3-D neighborhood attention, B=1 T={_g[0]} Y={_g[1]} X={_g[2]} H={_h} "
+                    f"D=64, window {_k[0]}x{_k[1]}x{_k[2]}, Q ~ N(0,1/64) (pre-scaled), "
+                    f"K, V ~ N(0,1), scale 1"))
 
 BY_NAME = {w.name: w for w in WORKLOADS}
 

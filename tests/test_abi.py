@@ -156,3 +156,29 @@ def test_python_block_causal_validates_before_the_library():
     x = torch.zeros(1, 4, 1, 128, dtype=torch.bfloat16)
     with pytest.raises((ValueError, TypeError)):
         attn.block_causal(x, x, x, torch.zeros(4, dtype=torch.int32))
+
+
+def na_call(q=A, k=A + 64 * MB, v=A + 128 * MB, out=A + 192 * MB, B=1, T=4, Y=8, X=40, H=4,
+            D=64, kt=3, ky=5, kx=7):
+    return attn.attn_na3d(q, k, v, out, B, T, Y, X, H, D, kt, ky, kx, None)
+
+
+def test_na3d_rejects_bad_arguments():
+    assert na_call(q=None) == -1 and na_call(v=None) == -1 and na_call(out=None) == -1
+    assert na_call(B=0) == -2 and na_call(T=0) == -2 and na_call(X=-1) == -2 and na_call(H=0) == -2
+    assert na_call(kt=2) == -2 and na_call(ky=0) == -2 and na_call(kx=8) == -2  # even / empty
+    assert na_call(kt=5) == -2 and na_call(ky=9) == -2 and na_call(X=5) == -2   # longer than axis
+    assert na_call(D=128) == -3
+    assert na_call(X=64, kx=35) == -3            # window wider than a tile allows
+    assert na_call(k=A + 64 * MB + 2) == -4
+    assert na_call(out=A + 1024) == -5            # output over q
+    assert na_call(X=1 << 16, H=1 << 10, kx=3) == -6
+
+
+def test_python_na3d_validates_before_the_library():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 2, 2, 2, 1, 64, dtype=torch.bfloat16)
+    with pytest.raises((ValueError, TypeError)):
+        attn.na3d(x, x, x, (1, 1, 1))  # CPU tensors are rejected
+    with pytest.raises((ValueError, TypeError)):
+        attn.na3d(x[0], x[0], x[0], (1, 1, 1))

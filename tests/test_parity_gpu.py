@@ -238,6 +238,9 @@ def test_workload_full_size(idx):
     say(f"workload {w.name}: generating inputs")
     ts = w.tensors()
     say(f"workload {w.name}: GPU call")
+    if w.kind == "na3d":
+        check_na3d_full_size(w, ts, idx)
+        return
     if w.kind == "block_causal":
         dts = [dev(t) for t in ts[:3]] + [torch.from_numpy(ts[3]).cuda()]
         out = attn.block_causal(*dts)
@@ -266,6 +269,62 @@ def test_workload_full_size(idx):
     sel = got if rows is None else got[rows]
     res = assert_accepted(sel, ref, w.name)
     say(f"workload {w.name}: {res}")
+
+
+def check_na3d_full_size(w, ts, idx):
+    dts = [dev(t) for t in ts]
+    out = attn.na3d(*dts, w.kernel)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out.float()).all())
+    # convex combination of values: within the per-(b, h, d) range of V over the volume
+    vf = dts[2].float().flatten(1, 3)
+    vmin, vmax = vf.amin(dim=1), vf.amax(dim=1)
+    o = out.float().flatten(1, 3)
+    assert bool((o >= vmin[:, None] - 1e-2).all()) and bool((o <= vmax[:, None] + 1e-2).all())
+    got = host(out).reshape(-1, w.D)
+    say(f"workload {w.name}: oracle rows")
+    rows = sample_rows(w, 3000, 800 + idx)
+    ref = oracle.na3d_rows(ts[0], ts[1], ts[2], w.kernel, rows=rows)
+    res = assert_accepted(got[rows], ref, w.name)
+    say(f"workload {w.name}: {res}")
+
+
+# ---------------------------------------------------------------- 3-D neighborhood attention
+
+NA_CASES = [
+    # (B, T, Y, X, H, (kt, ky, kx))
+    (1, 3, 5, 7, 4, (3, 3, 5)),      # one strip; windows moved inside at every border
+    (2, 4, 6, 40, 3, (3, 5, 7)),     # two strips, the second ragged; one idle wave
+    (1, 5, 9, 33, 5, (5, 7, 11)),    # a one-query strip; two head groups
+    (1, 2, 3, 64, 8, (1, 3, 1)),     # windows of one position on T and X
+    (1, 1, 2, 35, 2, (1, 1, 33)),    # the widest X window a tile holds
+    (1, 3, 3, 3, 4, (3, 3, 3)),      # the window covers the volume
+    (1, 2, 4, 97, 4, (1, 3, 9)),     # four strips, the last one query wide
+]
+
+
+@pytest.mark.parametrize("case", NA_CASES, ids=[f"{c[:5]}-{c[5]}" for c in NA_CASES])
+def test_na3d_small_all_elements(case):
+    B, T, Y, X, H, kernel = case
+    shape = (B, T, Y, X, H, 64)
+    say(f"na3d {case}")
+    seed = 1500 + 7 * sum(shape) + sum(kernel)
+    q = synth.normal_bf16(shape, seed, 0.5)
+    k = synth.normal_bf16(shape, seed + 1, 1.0)
+    v = synth.normal_bf16(shape, seed + 2, 1.0)
+    out = attn.na3d(dev(q), dev(k), dev(v), kernel)
+    ref = oracle.na3d_attention(q, k, v, kernel)
+    assert_accepted(host(out).reshape(-1, 64), ref.reshape(-1, 64), f"na3d {case}")
+
+
+def test_na3d_writes_only_its_output():
+    shape = (1, 2, 3, 40, 4, 64)
+    q, k, v = (dev(synth.normal_bf16(shape, 1600 + i, 1.0)) for i in range(3))
+    big = torch.full((3 * q.numel(),), 7.0, dtype=torch.bfloat16, device="cuda")
+    out = big[q.numel():2 * q.numel()].view(shape)
+    attn.na3d(q, k, v, (1, 3, 5), out=out)
+    torch.cuda.synchronize()
+    assert bool((big[:q.numel()] == 7.0).all()) and bool((big[2 * q.numel():] == 7.0).all())
 
 
 # ---------------------------------------------------------------- HIP graph capture

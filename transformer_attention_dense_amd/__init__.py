@@ -35,7 +35,8 @@ ERRORS = {
 }
 
 # Exported symbols, in header order.
-SYMBOLS = ("attn_dense", "attn_prefix", "attn_cross", "attn_block_causal", "attn_fwd_ex",
+SYMBOLS = ("attn_dense", "attn_prefix", "attn_cross", "attn_block_causal", "attn_na3d",
+           "attn_fwd_ex",
            "attn_plan", "attn_reserve_workspace", "attn_strerror", "attn_abi_version")
 
 
@@ -62,6 +63,7 @@ def library() -> ctypes.CDLL:
     lib.attn_prefix.argtypes = [p, p, p, p, p, p, i, i, i, i, i, p]
     lib.attn_cross.argtypes = [p, p, p, p, i, i, i, i, i, p]
     lib.attn_block_causal.argtypes = [p, p, p, p, p, i, i, i, i, p]
+    lib.attn_na3d.argtypes = [p, p, p, p] + [i] * 9 + [p]
     lib.attn_fwd_ex.argtypes = [p, p, p, i, p, p, i, p, i, i, i, i, i, i, p]
     lib.attn_plan.argtypes = [i, i, i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i),
                               ctypes.POINTER(ll), ctypes.POINTER(ll)]
@@ -92,6 +94,10 @@ def attn_cross(q, k, v, out, B, Nq, Nk, H, D, stream=0) -> int:
 
 def attn_block_causal(q, k, v, image_ids, out, B, N, H, D, stream=0) -> int:
     return library().attn_block_causal(q, k, v, image_ids, out, B, N, H, D, stream)
+
+
+def attn_na3d(q, k, v, out, B, T, Y, X, H, D, kt, ky, kx, stream=0) -> int:
+    return library().attn_na3d(q, k, v, out, B, T, Y, X, H, D, kt, ky, kx, stream)
 
 
 def attn_fwd_ex(q, k0, v0, n0, k1, v1, n1, out, B, Nq, H, D, num_splits=0, waves=0,
@@ -230,6 +236,31 @@ def block_causal(q, k, v, image_ids, out=None):
                            out.data_ptr(), B, N, H, D, _stream(q))
     if rc != ATTN_OK:
         raise AttnError(rc, "attn_block_causal")
+    return out
+
+
+def na3d(q, k, v, kernel, out=None):
+    """3-D neighborhood attention: q, k, v [B, T, Y, X, H, D] bf16 on the GPU, D = 64,
+    kernel = (kt, ky, kx) odd window sizes; scores are plain dot products (the model's
+    scale is in q)."""
+    import torch
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be a bfloat16 torch.Tensor")
+        if t.device.type != "cuda" or t.dim() != 6 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [B, T, Y, X, H, D] tensor on a GPU")
+        if tuple(t.shape) != tuple(q.shape) or t.device != q.device:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(q.shape)}")
+    B, T, Y, X, H, D = q.shape
+    kt, ky, kx = (int(x) for x in kernel)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    rc = attn_na3d(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, T, Y, X, H, D,
+                   kt, ky, kx, _stream(q))
+    if rc != ATTN_OK:
+        raise AttnError(rc, "attn_na3d")
     return out
 
 

@@ -10,7 +10,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn_dense.so")
 SOURCES = [os.path.join(CSRC, "attn_kernels.hip"), os.path.join(CSRC, "attn_pingpong.hip"),
-           os.path.join(CSRC, "attn_api.hip")]
+           os.path.join(CSRC, "attn_na3d.hip"), os.path.join(CSRC, "attn_api.hip")]
 
 # Packed FP32 VALU forms are disabled for all device code: the compiler otherwise
 # emits them from ordinary float code.

@@ -250,6 +250,45 @@ int run_block_causal(const void* q, const void* k, const void* v, const int* ids
     return ATTN_OK;
 }
 
+// 3-D neighborhood attention (attn_na3d.hip).
+int run_na3d(const void* q, const void* k, const void* v, void* out, int B, int T, int Y, int X,
+             int H, int D, int kt, int ky, int kx, void* stream) {
+    if (!q || !k || !v || !out) return ATTN_ERR_NULL;
+    if (B < 1 || T < 1 || Y < 1 || X < 1 || H < 1) return ATTN_ERR_SHAPE;
+    if (kt < 1 || ky < 1 || kx < 1 || kt % 2 == 0 || ky % 2 == 0 || kx % 2 == 0 || kt > T ||
+        ky > Y || kx > X)
+        return ATTN_ERR_SHAPE;
+    if (D != 64 || kx > 33) return ATTN_ERR_UNSUPPORTED;
+    const long long elems = (long long)B * T * Y * X * H * D;
+    // element offsets of whole rows fit in 32 bits per (b, t, y) row of X positions
+    if (elems >= (1LL << 40) || 2LL * X * H * D >= (1LL << 31) ||
+        (long long)B * T * Y * ((X + 31) / 32) * ((H + 3) / 4) >= (1LL << 31))
+        return ATTN_ERR_OVERFLOW;
+    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out)) return ATTN_ERR_ALIGN;
+    const long long bytes = 2 * elems;
+    if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) ||
+        overlaps(out, bytes, v, bytes))
+        return ATTN_ERR_ALIAS;
+    attn::NaParams p;
+    p.q = static_cast<const uint16_t*>(q);
+    p.k = static_cast<const uint16_t*>(k);
+    p.v = static_cast<const uint16_t*>(v);
+    p.out = static_cast<uint16_t*>(out);
+    p.B = B;
+    p.T = T;
+    p.Y = Y;
+    p.X = X;
+    p.H = H;
+    p.kt = kt;
+    p.ky = ky;
+    p.kx = kx;
+    p.strips = (X + 31) / 32;
+    p.hgroups = (H + 3) / 4;
+    if (attn::launch_na3d(p, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+        return ATTN_ERR_HIP;
+    return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -257,6 +296,11 @@ extern "C" {
 int attn_block_causal(const void* q, const void* k, const void* v, const int* image_ids,
                       void* out, int B, int N, int H, int D, void* stream) {
     return run_block_causal(q, k, v, image_ids, out, B, N, H, D, stream);
+}
+
+int attn_na3d(const void* q, const void* k, const void* v, void* out, int B, int T, int Y, int X,
+              int H, int D, int kt, int ky, int kx, void* stream) {
+    return run_na3d(q, k, v, out, B, T, Y, X, H, D, kt, ky, kx, stream);
 }
 
 int attn_dense(const void* q, const void* k, const void* v, void* out, int B, int N, int H,

@@ -42,6 +42,21 @@ struct CombineParams {
     int splits;
 };
 
+// Arguments of the 3-D neighborhood attention kernel (attn_na3d.hip), D = 64. All
+// tensors [B, T, Y, X, H, D] BF16 bits; windows (kt, ky, kx) odd and at most their axes.
+struct NaParams {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    uint16_t* out;
+    int B, T, Y, X, H;
+    int kt, ky, kx;
+    int strips;   // ceil(X / 32): 32-query strips on the X axis
+    int hgroups;  // ceil(H / 4): four heads per workgroup
+};
+long long na3d_workgroups(const NaParams& p);
+hipError_t launch_na3d(const NaParams& p, hipStream_t stream);
+
 // Keys per tile of the forward kernels; split ranges are multiples of it.
 constexpr int kKeyTile = 64;
 

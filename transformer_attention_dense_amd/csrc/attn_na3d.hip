@@ -1,0 +1,274 @@
+// 3-D neighborhood attention forward kernel for MI355X (gfx950), D = 64 (page "Audit
+// SGLang interfaces and refresh validated kernel solutions",
+// definitions/neighborhood_attention/neighborhood_attention_3d_*: natten's na3d with
+// kernel (kt, ky, kx) and scale 1, Q already scaled, layout [B, T, Y, X, H, D]; the
+// neighborhood is NATTEN's: on each axis an odd window centred on the query, moved
+// inside the axis at its ends).
+//
+// One wave owns 32 queries that are consecutive on the X axis at one (b, t, y, h); the
+// four waves of a workgroup are four heads of the same strip, so their loads share
+// cache lines. Every (t', y') row of the strip's window is a run of consecutive
+// positions on X, and the strip's windows on X all lie in the 64 positions starting
+// at the window of its first query (a window is at most 33 wide). So the wave walks
+// the kt*ky rows as 64-key tiles, exactly like the dense kernels walk key tiles:
+//
+//   * copy the K and V tile of the row into the wave's own LDS region
+//     (global_load_lds_dwordx4, scalar base + per-lane offsets fixed for the wave;
+//     positions past the end of the X axis are clamped and never visible);
+//   * S^T = K Q^T with 32x32x16 BF16 MFMAs (S in FP32), every key outside its query's
+//     X window set to -inf (the T and Y windows are the rows walked);
+//   * online softmax in the exp2 domain (scale 1, so c = log2 e), P rounded to BF16;
+//   * O^T += V^T P^T with the V operand read transposed from LDS (ds_read_b64_tr_b16).
+//
+// The LDS region of a wave is private, so the kernel has no barriers: a wave waits
+// for its own copies (vmcnt) before reading a tile and for its own reads (lgkmcnt)
+// before the next copies overwrite it. The other waves of the CU hide the latency.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "attn_device.h"
+#include "attn_launch.h"
+
+namespace attn {
+namespace {
+
+using namespace dev;
+
+// start of the window of odd size k around i on an axis of length L (k <= L)
+__device__ __forceinline__ int na_start(int i, int k, int L) {
+    return max(0, min(i - k / 2, L - k));
+}
+
+// s_waitcnt with only the vector-memory counter bounded (0), or only the LDS counter.
+__device__ __forceinline__ void wait_copies() {
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((0 & 15) | (0 << 14) | (7 << 4) | (15 << 8));
+    __asm__ volatile("" ::: "memory");
+}
+__device__ __forceinline__ void wait_lds_reads() {
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
+    __asm__ volatile("" ::: "memory");
+}
+
+constexpr int kNaWaves = 4;   // heads per workgroup
+constexpr int kNaStrip = 32;  // queries per wave, consecutive on X
+
+__global__ __launch_bounds__(256) void attn_na3d_kernel(NaParams p) {
+    constexpr int D = 64;
+    constexpr int KS = D / 16;       // MFMA k-steps over the head dim
+    constexpr int DB = D / 32;       // 32-wide head-dim blocks of O^T
+    constexpr int CPR = D / 8;       // 16-byte chunks per row
+    constexpr int ROWB = 2 * D;      // bytes per LDS row
+    constexpr int BN = 64;           // keys per tile
+    constexpr int NB = BN / 32;      // 32-key blocks per tile
+    constexpr int TILEB = BN * ROWB; // bytes per K or V tile
+    constexpr int ROUNDS = BN * CPR / kWave;  // 16-byte copies per lane per tile
+    constexpr int RROWS = kWave / CPR;        // rows per copy round
+    constexpr int NPAIR = NB * 8;    // exp pairs per lane per tile
+
+    __shared__ __attribute__((aligned(1024))) char smem[kNaWaves * 2 * TILEB];
+
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int n = lane & 31;
+    const int g = lane >> 5;
+
+    // workgroup -> (b, t, y, strip, head group)
+    long idx = blockIdx.x;
+    const int hg = (int)(idx % p.hgroups);
+    idx /= p.hgroups;
+    const int strip = (int)(idx % p.strips);
+    idx /= p.strips;
+    const int y = (int)(idx % p.Y);
+    idx /= p.Y;
+    const int t = (int)(idx % p.T);
+    const int b = (int)(idx / p.T);
+    const int h = hg * kNaWaves + wave;
+    if (h >= p.H) return;  // no barriers in this kernel
+
+    const int X = p.X;
+    const long HD = (long)p.H * D;
+    const int xq = strip * kNaStrip + n;  // this lane's query on X
+    const bool qvalid = xq < X;
+    const int xqc = min(xq, X - 1);
+    const long pos_q = (((long)b * p.T + t) * p.Y + y) * X + xqc;
+
+    // Q^T fragments (B operand): lane holds query n, dims 16*ks + 8g .. +7
+    bf16x8 qf[KS];
+    {
+        const uint16_t* qrow = p.q + pos_q * HD + (long)h * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks + 8 * g);
+    }
+
+    // windows: T and Y rows walked by the wave, X per query
+    const int t0 = na_start(t, p.kt, p.T);
+    const int y0 = na_start(y, p.ky, p.Y);
+    const int xs_q = na_start(xqc, p.kx, X);
+    const int xa = na_start(strip * kNaStrip, p.kx, X);  // first key position of a tile
+
+    char* const kt_lds = smem + wave * 2 * TILEB;
+    char* const vt_lds = kt_lds + TILEB;
+
+    // Loader: round i of lane l fills physical chunk 64 i + l of the tile: row
+    // r = RROWS i + l / CPR, position l % CPR holding logical chunk
+    // (l % CPR) ^ swizzle(r); the source position xa + r is clamped to the axis.
+    unsigned ld_off[ROUNDS];
+#pragma unroll
+    for (int i = 0; i < ROUNDS; ++i) {
+        const int r = RROWS * i + lane / CPR;
+        const int xk = min(xa + r, X - 1);
+        const int chunk = (lane % CPR) ^ lds_swizzle<CPR>(r);
+        ld_off[i] = (unsigned)(2 * ((long)xk * HD + chunk * 8));
+    }
+    // byte offset of (b, t', y', x = 0, h) in K or V
+    auto row_base = [&](int tt, int yy) {
+        return ((((long)b * p.T + tt) * p.Y + yy) * X * HD + (long)h * D) * 2;
+    };
+
+    // Per-lane LDS byte offsets: K operand reads per k-step, V transpose reads per
+    // head-dim block and 8-key half (as in the dense kernels).
+    int koff[KS];
+    {
+        const int tsw = lds_swizzle<CPR>(n) ^ g;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) koff[ks] = n * ROWB + 16 * ((2 * ks) ^ tsw);
+    }
+    int voff[DB][2];
+    {
+        const int tr_r = (lane & 15) >> 2;
+        const int tr_q = lane & 3;
+        const int half = (lane >> 4) & 1;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const int row = 8 * h2 + 4 * g + tr_r;
+                const int c = (4 * db + 2 * half + (tr_q >> 1)) ^ lds_swizzle<CPR>(row);
+                voff[db][h2] = row * ROWB + 16 * c + 8 * (tr_q & 1);
+            }
+    }
+    auto read_v = [&](int j) __attribute__((always_inline)) {
+        const int cc = j / DB, kb = cc / 2, tt = cc % 2, db = j % DB;
+        const int rowbase = (kb * 32 + 16 * tt) * ROWB;
+        const i16x4 lo =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt_lds + voff[db][0] + rowbase));
+        const i16x4 hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt_lds + voff[db][1] + rowbase));
+        const i16x8 a16 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        return __builtin_bit_cast(bf16x8, a16);
+    };
+
+    f32x16 o[DB];
+#pragma unroll
+    for (int i = 0; i < DB; ++i) o[i] = f32x16{};
+    float m_ref = -INFINITY;
+    float l_part = 0.f;
+    const float c = 1.4426950408889634f;  // log2(e): scale 1
+
+    const char* kbase = reinterpret_cast<const char*>(uniform_ptr(p.k));
+    const char* vbase = reinterpret_cast<const char*>(uniform_ptr(p.v));
+    for (int tt = t0; tt < t0 + p.kt; ++tt) {
+        for (int yy = y0; yy < y0 + p.ky; ++yy) {
+            // ---- copy the row's K and V tile (the previous tile's reads are done)
+            wait_lds_reads();
+            const long rb = row_base(tt, yy);
+#pragma unroll
+            for (int i = 0; i < ROUNDS; ++i)
+                load16_to_lds_sbase(kbase + rb, ld_off[i], kt_lds + i * kWave * 16);
+#pragma unroll
+            for (int i = 0; i < ROUNDS; ++i)
+                load16_to_lds_sbase(vbase + rb, ld_off[i], vt_lds + i * kWave * 16);
+            wait_copies();
+
+            // ---- S^T = K Q^T
+            f32x16 s[NB];
+#pragma unroll
+            for (int kb = 0; kb < NB; ++kb) {
+                s[kb] = f32x16{};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const bf16x8 a =
+                        *reinterpret_cast<const bf16x8*>(kt_lds + koff[ks] + kb * 32 * ROWB);
+                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
+                }
+            }
+            // ---- keys outside the query's X window are hidden
+#pragma unroll
+            for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int xk = xa + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+                    if (xk < xs_q || xk >= xs_q + p.kx) s[kb][r] = -INFINITY;
+                }
+            // ---- online softmax: running maximum raised only when a row's tile maximum
+            // exceeds it by more than 2^kRescaleLog2 in the exp2 domain
+            float mx = s[0][0];
+#pragma unroll
+            for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+            mx = wave_swap_max(mx);
+            const bool need = (mx - m_ref) * c > kRescaleLog2;
+            if (__builtin_amdgcn_ballot_w64(need) != 0) {
+                const float m_new = fmaxf(m_ref, mx);
+                const float alpha = (m_ref == -INFINITY) ? 0.f : exp2f((m_ref - m_new) * c);
+                l_part *= alpha;
+#pragma unroll
+                for (int i = 0; i < DB; ++i) o[i] *= alpha;
+                m_ref = m_new;
+            }
+            const float mc = m_ref * c;
+            bf16x8 pf[NB][2];
+            static_for<NPAIR>([&](auto pc) {
+                constexpr int pi = decltype(pc)::value;
+                constexpr int cc = pi / 4, kb = cc / 2, tt2 = cc % 2, r = 8 * tt2 + 2 * (pi % 4);
+                const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -mc));
+                const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r + 1], c, -mc));
+                const bf16x2 pk = {(__bf16)e0, (__bf16)e1};
+                l_part += e0 + e1;
+                pf[kb][tt2][r & 7] = pk[0];
+                pf[kb][tt2][(r & 7) + 1] = pk[1];
+            });
+            // ---- O^T += V^T P^T
+#pragma unroll
+            for (int j = 0; j < 2 * NB * DB; ++j) {
+                const int cc = j / DB, kb = cc / 2, tt2 = cc % 2, db = j % DB;
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_v(j), pf[kb][tt2], o[db], 0,
+                                                                0, 0);
+            }
+        }
+    }
+
+    // ---- epilogue
+    const float l_tot = wave_swap_sum(l_part);
+    if (!qvalid) return;
+    const float inv = 1.0f / l_tot;
+    uint16_t* orow = p.out + pos_q * HD + (long)h * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            bf16x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = (__bf16)(o[db][4 * j + e] * inv);
+            *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * j + 4 * g) = v;
+        }
+}
+
+}  // namespace
+
+long long na3d_workgroups(const NaParams& p) {
+    return (long long)p.B * p.T * p.Y * p.strips * p.hgroups;
+}
+
+hipError_t launch_na3d(const NaParams& p, hipStream_t stream) {
+    hipLaunchKernelGGL(attn_na3d_kernel, dim3((unsigned)na3d_workgroups(p)), dim3(256), 0,
+                       stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace attn
