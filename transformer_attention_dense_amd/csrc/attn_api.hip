@@ -262,7 +262,7 @@ int run_na3d(const void* q, const void* k, const void* v, void* out, int B, int 
     const long long elems = (long long)B * T * Y * X * H * D;
     // element offsets of whole rows fit in 32 bits per (b, t, y) row of X positions
     if (elems >= (1LL << 40) || 2LL * X * H * D >= (1LL << 31) ||
-        (long long)B * T * Y * ((X + 31) / 32) * ((H + 3) / 4) >= (1LL << 31))
+        (long long)B * T * ((Y + 3) / 4) * ((X + 31) / 32) * H >= (1LL << 31))
         return ATTN_ERR_OVERFLOW;
     if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out)) return ATTN_ERR_ALIGN;
     const long long bytes = 2 * elems;
@@ -283,7 +283,7 @@ int run_na3d(const void* q, const void* k, const void* v, void* out, int B, int 
     p.ky = ky;
     p.kx = kx;
     p.strips = (X + 31) / 32;
-    p.hgroups = (H + 3) / 4;
+    p.yblocks = (Y + 3) / 4;
     if (attn::launch_na3d(p, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
         return ATTN_ERR_HIP;
     return ATTN_OK;

@@ -52,7 +52,7 @@ struct NaParams {
     int B, T, Y, X, H;
     int kt, ky, kx;
     int strips;   // ceil(X / 32): 32-query strips on the X axis
-    int hgroups;  // ceil(H / 4): four heads per workgroup
+    int yblocks;  // ceil(Y / 4): four query rows y per workgroup
 };
 long long na3d_workgroups(const NaParams& p);
 hipError_t launch_na3d(const NaParams& p, hipStream_t stream);

@@ -5,24 +5,23 @@
 // neighborhood is NATTEN's: on each axis an odd window centred on the query, moved
 // inside the axis at its ends).
 //
-// One wave owns 32 queries that are consecutive on the X axis at one (b, t, y, h); the
-// four waves of a workgroup are four heads of the same strip, so their loads share
-// cache lines. Every (t', y') row of the strip's window is a run of consecutive
-// positions on X, and the strip's windows on X all lie in the 64 positions starting
-// at the window of its first query (a window is at most 33 wide). So the wave walks
-// the kt*ky rows as 64-key tiles, exactly like the dense kernels walk key tiles:
+// A workgroup owns four query strips: 32 consecutive positions on the X axis at one
+// (b, t, h), for four consecutive rows y (one wave each). Every (t', y') row of a
+// strip's window is a run of consecutive positions on X, and all windows of the
+// workgroup on X lie in the 64 positions starting at the window of its first query (a
+// window is at most 33 wide). The workgroup walks the union of its four windows on Y
+// (ky + 3 rows for interior strips) for each t' of the common T window, as 64-key
+// tiles streamed through a three-slot LDS ring exactly like the dense kernels stream
+// key tiles; each tile is copied once and used by every wave whose own Y window
+// contains its row:
 //
-//   * copy the K and V tile of the row into the wave's own LDS region
-//     (global_load_lds_dwordx4, scalar base + per-lane offsets fixed for the wave;
-//     positions past the end of the X axis are clamped and never visible);
+//   * copy the K and V tile of the row (global_load_lds_dwordx4, scalar base +
+//     per-lane offsets fixed for the workgroup; positions past the end of the X axis
+//     are clamped and never visible), two tiles ahead of their use;
 //   * S^T = K Q^T with 32x32x16 BF16 MFMAs (S in FP32), every key outside its query's
-//     X window set to -inf (the T and Y windows are the rows walked);
+//     X window set to -inf;
 //   * online softmax in the exp2 domain (scale 1, so c = log2 e), P rounded to BF16;
 //   * O^T += V^T P^T with the V operand read transposed from LDS (ds_read_b64_tr_b16).
-//
-// The LDS region of a wave is private, so the kernel has no barriers: a wave waits
-// for its own copies (vmcnt) before reading a tile and for its own reads (lgkmcnt)
-// before the next copies overwrite it. The other waves of the CU hide the latency.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -39,19 +38,7 @@ __device__ __forceinline__ int na_start(int i, int k, int L) {
     return max(0, min(i - k / 2, L - k));
 }
 
-// s_waitcnt with only the vector-memory counter bounded (0), or only the LDS counter.
-__device__ __forceinline__ void wait_copies() {
-    __asm__ volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt((0 & 15) | (0 << 14) | (7 << 4) | (15 << 8));
-    __asm__ volatile("" ::: "memory");
-}
-__device__ __forceinline__ void wait_lds_reads() {
-    __asm__ volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
-    __asm__ volatile("" ::: "memory");
-}
-
-constexpr int kNaWaves = 4;   // heads per workgroup
+constexpr int kNaWaves = 4;   // query rows y per workgroup (one wave each)
 constexpr int kNaStrip = 32;  // queries per wave, consecutive on X
 
 __global__ __launch_bounds__(256) void attn_na3d_kernel(NaParams p) {
@@ -63,11 +50,14 @@ __global__ __launch_bounds__(256) void attn_na3d_kernel(NaParams p) {
     constexpr int BN = 64;           // keys per tile
     constexpr int NB = BN / 32;      // 32-key blocks per tile
     constexpr int TILEB = BN * ROWB; // bytes per K or V tile
-    constexpr int ROUNDS = BN * CPR / kWave;  // 16-byte copies per lane per tile
-    constexpr int RROWS = kWave / CPR;        // rows per copy round
+    constexpr int NT = kNaWaves * kWave;
+    constexpr int PER_T = BN * CPR / NT;  // 16-byte copies per thread per tensor per tile
+    constexpr int RSTEP = NT / CPR;       // rows per copy round
+    constexpr int NSLOT = 3;
     constexpr int NPAIR = NB * 8;    // exp pairs per lane per tile
+    static_assert(RSTEP % 16 == 0, "loader pattern");
 
-    __shared__ __attribute__((aligned(1024))) char smem[kNaWaves * 2 * TILEB];
+    __shared__ __attribute__((aligned(1024))) char smem[NSLOT * 2 * TILEB];
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
@@ -75,25 +65,26 @@ __global__ __launch_bounds__(256) void attn_na3d_kernel(NaParams p) {
     const int n = lane & 31;
     const int g = lane >> 5;
 
-    // workgroup -> (b, t, y, strip, head group)
+    // workgroup -> (b, t, block of four rows y, strip, h), h fastest
     long idx = blockIdx.x;
-    const int hg = (int)(idx % p.hgroups);
-    idx /= p.hgroups;
+    const int h = (int)(idx % p.H);
+    idx /= p.H;
     const int strip = (int)(idx % p.strips);
     idx /= p.strips;
-    const int y = (int)(idx % p.Y);
-    idx /= p.Y;
+    const int yblk = (int)(idx % p.yblocks);
+    idx /= p.yblocks;
     const int t = (int)(idx % p.T);
     const int b = (int)(idx / p.T);
-    const int h = hg * kNaWaves + wave;
-    if (h >= p.H) return;  // no barriers in this kernel
 
-    const int X = p.X;
+    const int X = p.X, Y = p.Y;
     const long HD = (long)p.H * D;
-    const int xq = strip * kNaStrip + n;  // this lane's query on X
-    const bool qvalid = xq < X;
+    const int y = yblk * kNaWaves + wave;  // this wave's query row
+    const bool active = y < Y;
+    const int yc = min(y, Y - 1);
+    const int xq = strip * kNaStrip + n;   // this lane's query on X
+    const bool qvalid = active && xq < X;
     const int xqc = min(xq, X - 1);
-    const long pos_q = (((long)b * p.T + t) * p.Y + y) * X + xqc;
+    const long pos_q = (((long)b * p.T + t) * Y + yc) * X + xqc;
 
     // Q^T fragments (B operand): lane holds query n, dims 16*ks + 8g .. +7
     bf16x8 qf[KS];
@@ -104,29 +95,45 @@ __global__ __launch_bounds__(256) void attn_na3d_kernel(NaParams p) {
             qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks + 8 * g);
     }
 
-    // windows: T and Y rows walked by the wave, X per query
+    // windows: T common to the workgroup, Y per wave, X per query
     const int t0 = na_start(t, p.kt, p.T);
-    const int y0 = na_start(y, p.ky, p.Y);
+    const int ys = na_start(yc, p.ky, Y);
     const int xs_q = na_start(xqc, p.kx, X);
     const int xa = na_start(strip * kNaStrip, p.kx, X);  // first key position of a tile
+    // rows y' walked: the union of the four waves' windows
+    const int yu0 = na_start(yblk * kNaWaves, p.ky, Y);
+    const int yu1 = na_start(min(yblk * kNaWaves + kNaWaves - 1, Y - 1), p.ky, Y) + p.ky;
+    const int nyu = yu1 - yu0;
+    const int ntiles = p.kt * nyu;
 
-    char* const kt_lds = smem + wave * 2 * TILEB;
-    char* const vt_lds = kt_lds + TILEB;
-
-    // Loader: round i of lane l fills physical chunk 64 i + l of the tile: row
-    // r = RROWS i + l / CPR, position l % CPR holding logical chunk
-    // (l % CPR) ^ swizzle(r); the source position xa + r is clamped to the axis.
-    unsigned ld_off[ROUNDS];
+    // Loader: copy round i of thread tid fills physical chunk i*NT + tid of a tile:
+    // row r = RSTEP i + tid / CPR, position tid % CPR holding logical chunk
+    // (tid % CPR) ^ swizzle(r) (the same for every round: RSTEP is a multiple of the
+    // swizzle period); the source position xa + r is clamped to the axis.
+    unsigned ld_off[PER_T];
 #pragma unroll
-    for (int i = 0; i < ROUNDS; ++i) {
-        const int r = RROWS * i + lane / CPR;
+    for (int i = 0; i < PER_T; ++i) {
+        const int r = RSTEP * i + tid / CPR;
         const int xk = min(xa + r, X - 1);
-        const int chunk = (lane % CPR) ^ lds_swizzle<CPR>(r);
+        const int chunk = (tid % CPR) ^ lds_swizzle<CPR>(r);
         ld_off[i] = (unsigned)(2 * ((long)xk * HD + chunk * 8));
     }
-    // byte offset of (b, t', y', x = 0, h) in K or V
-    auto row_base = [&](int tt, int yy) {
-        return ((((long)b * p.T + tt) * p.Y + yy) * X * HD + (long)h * D) * 2;
+    const char* kbase = reinterpret_cast<const char*>(uniform_ptr(p.k));
+    const char* vbase = reinterpret_cast<const char*>(uniform_ptr(p.v));
+    auto kslot = [&](int j) { return smem + j * 2 * TILEB; };
+    auto vslot = [&](int j) { return smem + j * 2 * TILEB + TILEB; };
+    // tile i: row (t0 + i / nyu, yu0 + i % nyu) into slot i % NSLOT
+    auto issue_tile = [&](int i) {
+        const int tt = t0 + i / nyu, yy = yu0 + i % nyu;
+        const long rb = ((((long)b * p.T + tt) * Y + yy) * X * HD + (long)h * D) * 2;
+        char* const kd = kslot(i % NSLOT) + wave * kWave * 16;
+        char* const vd = vslot(i % NSLOT) + wave * kWave * 16;
+#pragma unroll
+        for (int r = 0; r < PER_T; ++r)
+            load16_to_lds_sbase(kbase + rb, ld_off[r], kd + r * NT * 16);
+#pragma unroll
+        for (int r = 0; r < PER_T; ++r)
+            load16_to_lds_sbase(vbase + rb, ld_off[r], vd + r * NT * 16);
     };
 
     // Per-lane LDS byte offsets: K operand reads per k-step, V transpose reads per
@@ -151,16 +158,6 @@ __global__ __launch_bounds__(256) void attn_na3d_kernel(NaParams p) {
                 voff[db][h2] = row * ROWB + 16 * c + 8 * (tr_q & 1);
             }
     }
-    auto read_v = [&](int j) __attribute__((always_inline)) {
-        const int cc = j / DB, kb = cc / 2, tt = cc % 2, db = j % DB;
-        const int rowbase = (kb * 32 + 16 * tt) * ROWB;
-        const i16x4 lo =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt_lds + voff[db][0] + rowbase));
-        const i16x4 hi =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt_lds + voff[db][1] + rowbase));
-        const i16x8 a16 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        return __builtin_bit_cast(bf16x8, a16);
-    };
 
     f32x16 o[DB];
 #pragma unroll
@@ -169,81 +166,93 @@ __global__ __launch_bounds__(256) void attn_na3d_kernel(NaParams p) {
     float l_part = 0.f;
     const float c = 1.4426950408889634f;  // log2(e): scale 1
 
-    const char* kbase = reinterpret_cast<const char*>(uniform_ptr(p.k));
-    const char* vbase = reinterpret_cast<const char*>(uniform_ptr(p.v));
-    for (int tt = t0; tt < t0 + p.kt; ++tt) {
-        for (int yy = y0; yy < y0 + p.ky; ++yy) {
-            // ---- copy the row's K and V tile (the previous tile's reads are done)
-            wait_lds_reads();
-            const long rb = row_base(tt, yy);
+    // The X window of a query covers the same keys of every tile (the tiles share
+    // their X positions): keys outside it get -inf added, one add per score.
+    f32x16 xmask[NB];
 #pragma unroll
-            for (int i = 0; i < ROUNDS; ++i)
-                load16_to_lds_sbase(kbase + rb, ld_off[i], kt_lds + i * kWave * 16);
+    for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
-            for (int i = 0; i < ROUNDS; ++i)
-                load16_to_lds_sbase(vbase + rb, ld_off[i], vt_lds + i * kWave * 16);
-            wait_copies();
+        for (int r = 0; r < 16; ++r) {
+            const int xk = xa + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+            xmask[kb][r] = (xk < xs_q || xk >= xs_q + p.kx) ? -INFINITY : 0.f;
+        }
 
-            // ---- S^T = K Q^T
-            f32x16 s[NB];
+    auto compute = [&](const char* kt_lds, const char* vt_lds) {
+        // ---- S^T = K Q^T
+        f32x16 s[NB];
 #pragma unroll
-            for (int kb = 0; kb < NB; ++kb) {
-                s[kb] = f32x16{};
+        for (int kb = 0; kb < NB; ++kb) {
+            s[kb] = f32x16{};
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const bf16x8 a =
-                        *reinterpret_cast<const bf16x8*>(kt_lds + koff[ks] + kb * 32 * ROWB);
-                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
-                }
-            }
-            // ---- keys outside the query's X window are hidden
-#pragma unroll
-            for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int xk = xa + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-                    if (xk < xs_q || xk >= xs_q + p.kx) s[kb][r] = -INFINITY;
-                }
-            // ---- online softmax: running maximum raised only when a row's tile maximum
-            // exceeds it by more than 2^kRescaleLog2 in the exp2 domain
-            float mx = s[0][0];
-#pragma unroll
-            for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-            mx = wave_swap_max(mx);
-            const bool need = (mx - m_ref) * c > kRescaleLog2;
-            if (__builtin_amdgcn_ballot_w64(need) != 0) {
-                const float m_new = fmaxf(m_ref, mx);
-                const float alpha = (m_ref == -INFINITY) ? 0.f : exp2f((m_ref - m_new) * c);
-                l_part *= alpha;
-#pragma unroll
-                for (int i = 0; i < DB; ++i) o[i] *= alpha;
-                m_ref = m_new;
-            }
-            const float mc = m_ref * c;
-            bf16x8 pf[NB][2];
-            static_for<NPAIR>([&](auto pc) {
-                constexpr int pi = decltype(pc)::value;
-                constexpr int cc = pi / 4, kb = cc / 2, tt2 = cc % 2, r = 8 * tt2 + 2 * (pi % 4);
-                const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -mc));
-                const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r + 1], c, -mc));
-                const bf16x2 pk = {(__bf16)e0, (__bf16)e1};
-                l_part += e0 + e1;
-                pf[kb][tt2][r & 7] = pk[0];
-                pf[kb][tt2][(r & 7) + 1] = pk[1];
-            });
-            // ---- O^T += V^T P^T
-#pragma unroll
-            for (int j = 0; j < 2 * NB * DB; ++j) {
-                const int cc = j / DB, kb = cc / 2, tt2 = cc % 2, db = j % DB;
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_v(j), pf[kb][tt2], o[db], 0,
-                                                                0, 0);
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 a =
+                    *reinterpret_cast<const bf16x8*>(kt_lds + koff[ks] + kb * 32 * ROWB);
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
             }
         }
+        // ---- keys outside the query's X window are hidden
+#pragma unroll
+        for (int kb = 0; kb < NB; ++kb) s[kb] += xmask[kb];
+        // ---- online softmax: running maximum raised only when a row's tile maximum
+        // exceeds it by more than 2^kRescaleLog2 in the exp2 domain
+        float mx = s[0][0];
+#pragma unroll
+        for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+        mx = wave_swap_max(mx);
+        const bool need = (mx - m_ref) * c > kRescaleLog2;
+        if (__builtin_amdgcn_ballot_w64(need) != 0) {
+            const float m_new = fmaxf(m_ref, mx);
+            const float alpha = (m_ref == -INFINITY) ? 0.f : exp2f((m_ref - m_new) * c);
+            l_part *= alpha;
+#pragma unroll
+            for (int i = 0; i < DB; ++i) o[i] *= alpha;
+            m_ref = m_new;
+        }
+        const float mc = m_ref * c;
+        bf16x8 pf[NB][2];
+        static_for<NPAIR>([&](auto pc) {
+            constexpr int pi = decltype(pc)::value;
+            constexpr int cc = pi / 4, kb = cc / 2, tt2 = cc % 2, r = 8 * tt2 + 2 * (pi % 4);
+            const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -mc));
+            const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r + 1], c, -mc));
+            const bf16x2 pk = {(__bf16)e0, (__bf16)e1};
+            l_part += e0 + e1;
+            pf[kb][tt2][r & 7] = pk[0];
+            pf[kb][tt2][(r & 7) + 1] = pk[1];
+        });
+        // ---- O^T += V^T P^T
+#pragma unroll
+        for (int j = 0; j < 2 * NB * DB; ++j) {
+            const int cc = j / DB, kb = cc / 2, tt2 = cc % 2, db = j % DB;
+            const int rowbase = (kb * 32 + 16 * tt2) * ROWB;
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4*)(vt_lds + voff[db][0] + rowbase));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4*)(vt_lds + voff[db][1] + rowbase));
+            const i16x8 a16 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a16),
+                                                            pf[kb][tt2], o[db], 0, 0, 0);
+        }
+    };
+
+    // ---- pipeline: tile i is copied two tiles ahead into slot i % 3; the barrier
+    // before tile i waits for its copies and lets the next tile's stay in flight
+    issue_tile(0);
+    if (ntiles > 1) issue_tile(1);
+    for (int i = 0; i < ntiles; ++i) {
+        if (i + 1 < ntiles)
+            barrier_vmcnt<2 * PER_T>();
+        else
+            barrier_vmcnt<0>();
+        if (i + 2 < ntiles) issue_tile(i + 2);  // into the slot tile i-1 left
+        const int yy = yu0 + i % nyu;
+        if (active && yy >= ys && yy < ys + p.ky) compute(kslot(i % NSLOT), vslot(i % NSLOT));
     }
 
     // ---- epilogue
+    if (!active) return;
     const float l_tot = wave_swap_sum(l_part);
     if (!qvalid) return;
     const float inv = 1.0f / l_tot;
@@ -262,7 +271,7 @@ __global__ __launch_bounds__(256) void attn_na3d_kernel(NaParams p) {
 }  // namespace
 
 long long na3d_workgroups(const NaParams& p) {
-    return (long long)p.B * p.T * p.Y * p.strips * p.hgroups;
+    return (long long)p.B * p.T * p.yblocks * p.strips * p.H;
 }
 
 hipError_t launch_na3d(const NaParams& p, hipStream_t stream) {
