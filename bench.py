@@ -200,9 +200,9 @@ def bench_one(w, steps, warmup, torch, attn):
     if w.kind == "block_causal":  # always one split of the 8-wave kernel
         plan = {"splits": 1, "waves": 8, "workgroups": -(-w.Nq // 256) * w.B * w.H,
                 "workspace_bytes": 16 * -(-w.Nq // 32), "block_causal": True}
-    elif w.kind == "na3d":  # one wave per 32-query strip, four rows y per workgroup
+    elif w.kind == "na3d":  # a wave = 2 rows y x 16 positions on X, 4 waves per workgroup
         T, Y, X = w.grid
-        plan = {"splits": 1, "waves": 4, "workgroups": w.B * T * -(-Y // 4) * -(-X // 32) * w.H,
+        plan = {"splits": 1, "waves": 4, "workgroups": w.B * T * -(-Y // 8) * -(-X // 16) * w.H,
                 "workspace_bytes": 0, "na3d": True}
     else:
         plan = attn.attn_plan(w.B, w.Nq, w.keys, w.H, w.D)

@@ -107,7 +107,7 @@ int attn_block_causal(const void* q, const void* k, const void* v, const int* im
  *   FP32, output rounded to BF16. The neighborhood is NATTEN's published one; the pages
  *   name na3d without defining it.
  * Errors: ATTN_ERR_SHAPE for a size < 1 or a window that is even or longer than its
- * axis; ATTN_ERR_UNSUPPORTED for D != 64 or kx > 33; ATTN_ERR_OVERFLOW, ATTN_ERR_ALIGN,
+ * axis; ATTN_ERR_UNSUPPORTED for D != 64 or kx > 17; ATTN_ERR_OVERFLOW, ATTN_ERR_ALIGN,
  * ATTN_ERR_ALIAS as for the other calls. No work space.
  */
 int attn_na3d(const void* q, const void* k, const void* v, void* out, int B, int T, int Y,

@@ -258,11 +258,11 @@ int run_na3d(const void* q, const void* k, const void* v, void* out, int B, int 
     if (kt < 1 || ky < 1 || kx < 1 || kt % 2 == 0 || ky % 2 == 0 || kx % 2 == 0 || kt > T ||
         ky > Y || kx > X)
         return ATTN_ERR_SHAPE;
-    if (D != 64 || kx > 33) return ATTN_ERR_UNSUPPORTED;
+    if (D != 64 || kx > 17) return ATTN_ERR_UNSUPPORTED;
     const long long elems = (long long)B * T * Y * X * H * D;
     // element offsets of whole rows fit in 32 bits per (b, t, y) row of X positions
     if (elems >= (1LL << 40) || 2LL * X * H * D >= (1LL << 31) ||
-        (long long)B * T * ((Y + 3) / 4) * ((X + 31) / 32) * H >= (1LL << 31))
+        (long long)B * T * ((Y + 7) / 8) * ((X + 15) / 16) * H >= (1LL << 31))
         return ATTN_ERR_OVERFLOW;
     if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out)) return ATTN_ERR_ALIGN;
     const long long bytes = 2 * elems;
@@ -282,8 +282,8 @@ int run_na3d(const void* q, const void* k, const void* v, void* out, int B, int 
     p.kt = kt;
     p.ky = ky;
     p.kx = kx;
-    p.strips = (X + 31) / 32;
-    p.yblocks = (Y + 3) / 4;
+    p.strips = (X + 15) / 16;
+    p.yblocks = (Y + 7) / 8;
     if (attn::launch_na3d(p, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
         return ATTN_ERR_HIP;
     return ATTN_OK;

@@ -51,8 +51,8 @@ struct NaParams {
     uint16_t* out;
     int B, T, Y, X, H;
     int kt, ky, kx;
-    int strips;   // ceil(X / 32): 32-query strips on the X axis
-    int yblocks;  // ceil(Y / 4): four query rows y per workgroup
+    int strips;   // ceil(X / 16): strips of 16 positions on the X axis
+    int yblocks;  // ceil(Y / 8): eight query rows y per workgroup
 };
 long long na3d_workgroups(const NaParams& p);
 hipError_t launch_na3d(const NaParams& p, hipStream_t stream);

@@ -5,21 +5,22 @@
 // neighborhood is NATTEN's: on each axis an odd window centred on the query, moved
 // inside the axis at its ends).
 //
-// A workgroup owns four query strips: 32 consecutive positions on the X axis at one
-// (b, t, h), for four consecutive rows y (one wave each). Every (t', y') row of a
-// strip's window is a run of consecutive positions on X, and all windows of the
-// workgroup on X lie in the 64 positions starting at the window of its first query (a
-// window is at most 33 wide). The workgroup walks the union of its four windows on Y
-// (ky + 3 rows for interior strips) for each t' of the common T window, as 64-key
-// tiles streamed through a three-slot LDS ring exactly like the dense kernels stream
-// key tiles; each tile is copied once and used by every wave whose own Y window
-// contains its row:
+// A wave owns 32 queries: 16 consecutive positions on the X axis in two consecutive
+// rows y, at one (b, t, h); a workgroup stacks four waves on Y (8 rows). Every (t', y')
+// row of a query's window is a run of consecutive positions on X, and the X windows of
+// the 16 positions lie in the 32 positions starting at the window of the first one (a
+// window is at most 17 wide), so one 32-key tile per row holds them all. The workgroup
+// walks the union of its eight rows' Y windows (ky + 7 rows for interior blocks) for
+// each t' of the common T window, as 32-key tiles streamed through a three-slot LDS
+// ring exactly like the dense kernels stream key tiles; each tile is copied once and
+// used by every wave whose rows' windows contain its row:
 //
 //   * copy the K and V tile of the row (global_load_lds_dwordx4, scalar base +
 //     per-lane offsets fixed for the workgroup; positions past the end of the X axis
 //     are clamped and never visible), two tiles ahead of their use;
-//   * S^T = K Q^T with 32x32x16 BF16 MFMAs (S in FP32), every key outside its query's
-//     X window set to -inf;
+//   * S^T = K Q^T with 32x32x16 BF16 MFMAs (S in FP32); per lane, keys outside its
+//     query's X window, and the whole tile when its row is outside the query's Y window,
+//     get -inf added;
 //   * online softmax in the exp2 domain (scale 1, so c = log2 e), P rounded to BF16;
 //   * O^T += V^T P^T with the V operand read transposed from LDS (ds_read_b64_tr_b16).
 #include <hip/hip_runtime.h>
@@ -38,8 +39,9 @@ __device__ __forceinline__ int na_start(int i, int k, int L) {
     return max(0, min(i - k / 2, L - k));
 }
 
-constexpr int kNaWaves = 4;   // query rows y per workgroup (one wave each)
-constexpr int kNaStrip = 32;  // queries per wave, consecutive on X
+constexpr int kNaWaves = 4;  // waves per workgroup, stacked on Y
+constexpr int kNaRows = 2;   // rows y per wave
+constexpr int kNaXs = 16;    // positions on X per wave
 
 __global__ __launch_bounds__(256) void attn_na3d_kernel(NaParams p) {
     constexpr int D = 64;
@@ -47,15 +49,13 @@ __global__ __launch_bounds__(256) void attn_na3d_kernel(NaParams p) {
     constexpr int DB = D / 32;       // 32-wide head-dim blocks of O^T
     constexpr int CPR = D / 8;       // 16-byte chunks per row
     constexpr int ROWB = 2 * D;      // bytes per LDS row
-    constexpr int BN = 64;           // keys per tile
-    constexpr int NB = BN / 32;      // 32-key blocks per tile
+    constexpr int BN = 32;           // keys per tile
     constexpr int TILEB = BN * ROWB; // bytes per K or V tile
     constexpr int NT = kNaWaves * kWave;
-    constexpr int PER_T = BN * CPR / NT;  // 16-byte copies per thread per tensor per tile
-    constexpr int RSTEP = NT / CPR;       // rows per copy round
+    static_assert(BN * CPR == NT, "one 16-byte copy per thread per tensor and tile");
     constexpr int NSLOT = 3;
-    constexpr int NPAIR = NB * 8;    // exp pairs per lane per tile
-    static_assert(RSTEP % 16 == 0, "loader pattern");
+    constexpr int NPAIR = 8;         // exp pairs per lane per tile
+    constexpr int YB = kNaWaves * kNaRows;  // rows y per workgroup
 
     __shared__ __attribute__((aligned(1024))) char smem[NSLOT * 2 * TILEB];
 
@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256) void attn_na3d_kernel(NaParams p) {
     const int n = lane & 31;
     const int g = lane >> 5;
 
-    // workgroup -> (b, t, block of four rows y, strip, h), h fastest
+    // workgroup -> (b, t, block of eight rows y, strip of 16 on X, h), h fastest
     long idx = blockIdx.x;
     const int h = (int)(idx % p.H);
     idx /= p.H;
@@ -78,13 +78,13 @@ __global__ __launch_bounds__(256) void attn_na3d_kernel(NaParams p) {
 
     const int X = p.X, Y = p.Y;
     const long HD = (long)p.H * D;
-    const int y = yblk * kNaWaves + wave;  // this wave's query row
-    const bool active = y < Y;
-    const int yc = min(y, Y - 1);
-    const int xq = strip * kNaStrip + n;   // this lane's query on X
-    const bool qvalid = active && xq < X;
-    const int xqc = min(xq, X - 1);
-    const long pos_q = (((long)b * p.T + t) * Y + yc) * X + xqc;
+    const int wy0 = yblk * YB + wave * kNaRows;  // the wave's first row y
+    const bool active = wy0 < Y;
+    const int yq = wy0 + (n >> 4);               // this lane's query row
+    const int xq = strip * kNaXs + (n & 15);     // and position on X
+    const bool qvalid = yq < Y && xq < X;
+    const int yqc = min(yq, Y - 1), xqc = min(xq, X - 1);
+    const long pos_q = (((long)b * p.T + t) * Y + yqc) * X + xqc;
 
     // Q^T fragments (B operand): lane holds query n, dims 16*ks + 8g .. +7
     bf16x8 qf[KS];
@@ -95,28 +95,28 @@ __global__ __launch_bounds__(256) void attn_na3d_kernel(NaParams p) {
             qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks + 8 * g);
     }
 
-    // windows: T common to the workgroup, Y per wave, X per query
+    // windows: T common to the workgroup, Y and X per query
     const int t0 = na_start(t, p.kt, p.T);
-    const int ys = na_start(yc, p.ky, Y);
+    const int ys_q = na_start(yqc, p.ky, Y);
     const int xs_q = na_start(xqc, p.kx, X);
-    const int xa = na_start(strip * kNaStrip, p.kx, X);  // first key position of a tile
-    // rows y' walked: the union of the four waves' windows
-    const int yu0 = na_start(yblk * kNaWaves, p.ky, Y);
-    const int yu1 = na_start(min(yblk * kNaWaves + kNaWaves - 1, Y - 1), p.ky, Y) + p.ky;
+    const int xa = na_start(strip * kNaXs, p.kx, X);  // first key position of a tile
+    // rows y' the wave needs (its two rows' windows) and the workgroup walks (eight)
+    const int wv0 = na_start(min(wy0, Y - 1), p.ky, Y);
+    const int wv1 = na_start(min(wy0 + kNaRows - 1, Y - 1), p.ky, Y) + p.ky;
+    const int yu0 = na_start(min(yblk * YB, Y - 1), p.ky, Y);
+    const int yu1 = na_start(min(yblk * YB + YB - 1, Y - 1), p.ky, Y) + p.ky;
     const int nyu = yu1 - yu0;
     const int ntiles = p.kt * nyu;
 
-    // Loader: copy round i of thread tid fills physical chunk i*NT + tid of a tile:
-    // row r = RSTEP i + tid / CPR, position tid % CPR holding logical chunk
-    // (tid % CPR) ^ swizzle(r) (the same for every round: RSTEP is a multiple of the
-    // swizzle period); the source position xa + r is clamped to the axis.
-    unsigned ld_off[PER_T];
-#pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
-        const int r = RSTEP * i + tid / CPR;
+    // Loader: thread tid copies physical chunk tid of a tile: row r = tid / CPR,
+    // position tid % CPR holding logical chunk (tid % CPR) ^ swizzle(r); the source
+    // position xa + r is clamped to the axis.
+    unsigned ld_off;
+    {
+        const int r = tid / CPR;
         const int xk = min(xa + r, X - 1);
         const int chunk = (tid % CPR) ^ lds_swizzle<CPR>(r);
-        ld_off[i] = (unsigned)(2 * ((long)xk * HD + chunk * 8));
+        ld_off = (unsigned)(2 * ((long)xk * HD + chunk * 8));
     }
     const char* kbase = reinterpret_cast<const char*>(uniform_ptr(p.k));
     const char* vbase = reinterpret_cast<const char*>(uniform_ptr(p.v));
@@ -126,14 +126,8 @@ __global__ __launch_bounds__(256) void attn_na3d_kernel(NaParams p) {
     auto issue_tile = [&](int i) {
         const int tt = t0 + i / nyu, yy = yu0 + i % nyu;
         const long rb = ((((long)b * p.T + tt) * Y + yy) * X * HD + (long)h * D) * 2;
-        char* const kd = kslot(i % NSLOT) + wave * kWave * 16;
-        char* const vd = vslot(i % NSLOT) + wave * kWave * 16;
-#pragma unroll
-        for (int r = 0; r < PER_T; ++r)
-            load16_to_lds_sbase(kbase + rb, ld_off[r], kd + r * NT * 16);
-#pragma unroll
-        for (int r = 0; r < PER_T; ++r)
-            load16_to_lds_sbase(vbase + rb, ld_off[r], vd + r * NT * 16);
+        load16_to_lds_sbase(kbase + rb, ld_off, kslot(i % NSLOT) + wave * kWave * 16);
+        load16_to_lds_sbase(vbase + rb, ld_off, vslot(i % NSLOT) + wave * kWave * 16);
     };
 
     // Per-lane LDS byte offsets: K operand reads per k-step, V transpose reads per
@@ -168,38 +162,30 @@ __global__ __launch_bounds__(256) void attn_na3d_kernel(NaParams p) {
 
     // The X window of a query covers the same keys of every tile (the tiles share
     // their X positions): keys outside it get -inf added, one add per score.
-    f32x16 xmask[NB];
+    f32x16 xmask;
 #pragma unroll
-    for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int xk = xa + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-            xmask[kb][r] = (xk < xs_q || xk >= xs_q + p.kx) ? -INFINITY : 0.f;
-        }
+    for (int r = 0; r < 16; ++r) {
+        const int xk = xa + 8 * (r >> 2) + 4 * g + (r & 3);
+        xmask[r] = (xk < xs_q || xk >= xs_q + p.kx) ? -INFINITY : 0.f;
+    }
 
-    auto compute = [&](const char* kt_lds, const char* vt_lds) {
+    auto compute = [&](const char* kt_lds, const char* vt_lds, int yy) {
         // ---- S^T = K Q^T
-        f32x16 s[NB];
+        f32x16 s = f32x16{};
 #pragma unroll
-        for (int kb = 0; kb < NB; ++kb) {
-            s[kb] = f32x16{};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 a =
-                    *reinterpret_cast<const bf16x8*>(kt_lds + koff[ks] + kb * 32 * ROWB);
-                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
-            }
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt_lds + koff[ks]);
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s, 0, 0, 0);
         }
-        // ---- keys outside the query's X window are hidden
-#pragma unroll
-        for (int kb = 0; kb < NB; ++kb) s[kb] += xmask[kb];
+        // ---- keys outside the query's window are hidden (a row outside its Y window
+        // hides the whole tile for that query)
+        const float ymask = (yy >= ys_q && yy < ys_q + p.ky) ? 0.f : -INFINITY;
+        s += xmask + ymask;
         // ---- online softmax: running maximum raised only when a row's tile maximum
         // exceeds it by more than 2^kRescaleLog2 in the exp2 domain
-        float mx = s[0][0];
+        float mx = s[0];
 #pragma unroll
-        for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
         mx = wave_swap_max(mx);
         const bool need = (mx - m_ref) * c > kRescaleLog2;
         if (__builtin_amdgcn_ballot_w64(need) != 0) {
@@ -210,30 +196,31 @@ __global__ __launch_bounds__(256) void attn_na3d_kernel(NaParams p) {
             for (int i = 0; i < DB; ++i) o[i] *= alpha;
             m_ref = m_new;
         }
-        const float mc = m_ref * c;
-        bf16x8 pf[NB][2];
+        // a query that has seen no key yet keeps m_ref = -inf; its scores are -inf too
+        const float mc = (m_ref == -INFINITY) ? 0.f : m_ref * c;
+        bf16x8 pf[2];
         static_for<NPAIR>([&](auto pc) {
             constexpr int pi = decltype(pc)::value;
-            constexpr int cc = pi / 4, kb = cc / 2, tt2 = cc % 2, r = 8 * tt2 + 2 * (pi % 4);
-            const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -mc));
-            const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r + 1], c, -mc));
+            constexpr int tt2 = pi / 4, r = 8 * tt2 + 2 * (pi % 4);
+            const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -mc));
+            const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 1], c, -mc));
             const bf16x2 pk = {(__bf16)e0, (__bf16)e1};
             l_part += e0 + e1;
-            pf[kb][tt2][r & 7] = pk[0];
-            pf[kb][tt2][(r & 7) + 1] = pk[1];
+            pf[tt2][r & 7] = pk[0];
+            pf[tt2][(r & 7) + 1] = pk[1];
         });
         // ---- O^T += V^T P^T
 #pragma unroll
-        for (int j = 0; j < 2 * NB * DB; ++j) {
-            const int cc = j / DB, kb = cc / 2, tt2 = cc % 2, db = j % DB;
-            const int rowbase = (kb * 32 + 16 * tt2) * ROWB;
+        for (int j = 0; j < 2 * DB; ++j) {
+            const int tt2 = j / DB, db = j % DB;
+            const int rowbase = 16 * tt2 * ROWB;
             const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (lds_i16x4*)(vt_lds + voff[db][0] + rowbase));
             const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (lds_i16x4*)(vt_lds + voff[db][1] + rowbase));
             const i16x8 a16 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
             o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a16),
-                                                            pf[kb][tt2], o[db], 0, 0, 0);
+                                                            pf[tt2], o[db], 0, 0, 0);
         }
     };
 
@@ -243,12 +230,13 @@ __global__ __launch_bounds__(256) void attn_na3d_kernel(NaParams p) {
     if (ntiles > 1) issue_tile(1);
     for (int i = 0; i < ntiles; ++i) {
         if (i + 1 < ntiles)
-            barrier_vmcnt<2 * PER_T>();
+            barrier_vmcnt<2>();
         else
             barrier_vmcnt<0>();
         if (i + 2 < ntiles) issue_tile(i + 2);  // into the slot tile i-1 left
         const int yy = yu0 + i % nyu;
-        if (active && yy >= ys && yy < ys + p.ky) compute(kslot(i % NSLOT), vslot(i % NSLOT));
+        if (active && yy >= wv0 && yy < wv1)
+            compute(kslot(i % NSLOT), vslot(i % NSLOT), yy);
     }
 
     // ---- epilogue
