@@ -38,19 +38,19 @@ METRIC = "attention TFLOP/s and % of MI355X bf16 MFMA peak, H=32 D=128 N=4096"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X published dense BF16 MFMA peak (2.5 PFLOP/s)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
 DEFAULT_WORKLOAD = "dense_b1_n4096_h32_d128"
-KERNEL_SOURCES = ["transformer_attention_dense_amd/csrc/attn_kernels.hip",
-                  "transformer_attention_dense_amd/csrc/attn_pingpong.hip",
-                  "transformer_attention_dense_amd/csrc/attn_na3d.hip",
-                  "transformer_attention_dense_amd/csrc/attn_device.h",
-                  "transformer_attention_dense_amd/csrc/attn_api.hip",
-                  "transformer_attention_dense_amd/csrc/attn_launch.h"]
+CSRC = "transformer_attention_dense_amd/csrc/"
+SHARED_SOURCES = ["attn_device.h", "attn_api.hip", "attn_launch.h"]
+KIND_SOURCES = {"na3d": ["attn_na3d.hip"]}
+DENSE_SOURCES = ["attn_kernels.hip", "attn_pingpong.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kind) -> str:
+    """Hash of the sources the kernels of one workload kind are built from: counter
+    readings taken on other sources are stale."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
+    for rel in SHARED_SOURCES + KIND_SOURCES.get(kind, DENSE_SOURCES):
+        with open(os.path.join(ROOT, CSRC, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -91,15 +91,15 @@ def make_call(w, dts, attn):
     return out, (lambda: attn.prefix(*dts, out=out))
 
 
-def traffic_for(workload_name):
+def traffic_for(w):
     """HBM bytes per launch from committed counter runs, if taken on this kernel source."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    entry = t.get("workloads", {}).get(workload_name)
-    if not entry or t.get("kernel_source_hash") != kernel_source_hash():
+    entry = t.get("workloads", {}).get(w.name)
+    if not entry or entry.get("kernel_source_hash") != kernel_source_hash(w.kind):
         return None
     return entry.get("hbm_bytes_per_launch")
 
@@ -229,7 +229,7 @@ def record(w, r, steps, warmup, cpu):
     value = w.flop * steps / r["wall_s"] / 1e12
     launch_us = r["event_ms"] * 1000.0 / steps  # average duration per launch on the stream
     achieved = w.flop / (launch_us * 1e-6) / 1e12
-    hbm = traffic_for(w.name)
+    hbm = traffic_for(w)
     rec = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -287,7 +287,7 @@ def _counter_means(csv_path, counter):
             if r["Counter_Name"] != counter:
                 continue
             name = r["Kernel_Name"]
-            if "attn_fwd" in name:
+            if "attn_fwd" in name or "attn_na3d" in name:
                 att.append(float(r["Counter_Value"]))
             elif "neg" in name:
                 cal.append(float(r["Counter_Value"]))
@@ -299,6 +299,7 @@ def _counter_means(csv_path, counter):
 def ingest(fetch_csv, write_csv, calib_mib, workload_name):
     """FETCH_SIZE and WRITE_SIZE are in KiB per dispatch; each is scaled by what the same
     counter reads for the calibration kernel, which moves exactly calib_mib MiB each way."""
+    import synth
     known = calib_mib * 1024.0  # KiB
     fa, fc = _counter_means(fetch_csv, "FETCH_SIZE")
     wa, wc = _counter_means(write_csv, "WRITE_SIZE")
@@ -309,9 +310,9 @@ def ingest(fetch_csv, write_csv, calib_mib, workload_name):
             t = json.load(f)
     except (OSError, ValueError):
         t = {}
-    if t.get("kernel_source_hash") != kernel_source_hash():
-        t = {"kernel_source_hash": kernel_source_hash(), "workloads": {}}
+    t.pop("kernel_source_hash", None)
     t.setdefault("workloads", {})[workload_name] = {
+        "kernel_source_hash": kernel_source_hash(synth.workload(workload_name).kind),
         "hbm_bytes_per_launch": round(hbm),
         "fetch_kib_raw": fa, "write_kib_raw": wa,
         "calibration": {"kib_each_way": known, "fetch_kib_read": fc, "write_kib_read": wc,

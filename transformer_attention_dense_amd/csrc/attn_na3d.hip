@@ -11,13 +11,13 @@
 // the 16 positions lie in the 32 positions starting at the window of the first one (a
 // window is at most 17 wide), so one 32-key tile per row holds them all. The workgroup
 // walks the union of its eight rows' Y windows (ky + 7 rows for interior blocks) for
-// each t' of the common T window, as 32-key tiles streamed through a three-slot LDS
+// each t' of the common T window, as 32-key tiles streamed through a four-slot LDS
 // ring exactly like the dense kernels stream key tiles; each tile is copied once and
 // used by every wave whose rows' windows contain its row:
 //
 //   * copy the K and V tile of the row (global_load_lds_dwordx4, scalar base +
 //     per-lane offsets fixed for the workgroup; positions past the end of the X axis
-//     are clamped and never visible), two tiles ahead of their use;
+//     are clamped and never visible), three tiles ahead of their use;
 //   * S^T = K Q^T with 32x32x16 BF16 MFMAs (S in FP32); per lane, keys outside its
 //     query's X window, and the whole tile when its row is outside the query's Y window,
 //     get -inf added;
@@ -39,11 +39,28 @@ __device__ __forceinline__ int na_start(int i, int k, int L) {
     return max(0, min(i - k / 2, L - k));
 }
 
+// Barrier after waiting for the copies of all but the min(left, K) most recently issued
+// tiles (two loads per tile: K and V); left is uniform.
+template <int K>
+__device__ __forceinline__ void barrier_tiles_left(int left) {
+    if constexpr (K == 0) {
+        barrier_vmcnt<0>();
+    } else {
+        if (left >= K)
+            barrier_vmcnt<2 * K>();
+        else
+            barrier_tiles_left<K - 1>(left);
+    }
+}
+
 constexpr int kNaWaves = 4;  // waves per workgroup, stacked on Y
 constexpr int kNaRows = 2;   // rows y per wave
 constexpr int kNaXs = 16;    // positions on X per wave
 
-__global__ __launch_bounds__(256) void attn_na3d_kernel(NaParams p) {
+// Four waves per SIMD (at most 128 VGPRs): the kernel is latency bound, and above 128
+// registers the compiler keeps the MFMA accumulators in AGPRs and copies them around.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
+void attn_na3d_kernel(NaParams p) {
     constexpr int D = 64;
     constexpr int KS = D / 16;       // MFMA k-steps over the head dim
     constexpr int DB = D / 32;       // 32-wide head-dim blocks of O^T
@@ -53,7 +70,8 @@ __global__ __launch_bounds__(256) void attn_na3d_kernel(NaParams p) {
     constexpr int TILEB = BN * ROWB; // bytes per K or V tile
     constexpr int NT = kNaWaves * kWave;
     static_assert(BN * CPR == NT, "one 16-byte copy per thread per tensor and tile");
-    constexpr int NSLOT = 3;
+    constexpr int NSLOT = 4;         // LDS ring slots
+    constexpr int AHEAD = NSLOT - 1; // tiles copied ahead of the one in use
     constexpr int NPAIR = 8;         // exp pairs per lane per tile
     constexpr int YB = kNaWaves * kNaRows;  // rows y per workgroup
 
@@ -224,16 +242,13 @@ __global__ __launch_bounds__(256) void attn_na3d_kernel(NaParams p) {
         }
     };
 
-    // ---- pipeline: tile i is copied two tiles ahead into slot i % 3; the barrier
-    // before tile i waits for its copies and lets the next tile's stay in flight
-    issue_tile(0);
-    if (ntiles > 1) issue_tile(1);
+    // ---- pipeline: tile i is copied AHEAD tiles ahead into slot i % NSLOT; the
+    // barrier before tile i waits for its copies and lets the later ones stay in flight
+    const int npre = min(AHEAD, ntiles);
+    for (int i = 0; i < npre; ++i) issue_tile(i);
     for (int i = 0; i < ntiles; ++i) {
-        if (i + 1 < ntiles)
-            barrier_vmcnt<2>();
-        else
-            barrier_vmcnt<0>();
-        if (i + 2 < ntiles) issue_tile(i + 2);  // into the slot tile i-1 left
+        barrier_tiles_left<AHEAD - 1>(ntiles - 1 - i);
+        if (i + AHEAD < ntiles) issue_tile(i + AHEAD);  // into the slot tile i-1 left
         const int yy = yu0 + i % nyu;
         if (active && yy >= wv0 && yy < wv1)
             compute(kslot(i % NSLOT), vslot(i % NSLOT), yy);
