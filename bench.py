@@ -200,9 +200,11 @@ def bench_one(w, steps, warmup, torch, attn):
     if w.kind == "block_causal":  # always one split of the 8-wave kernel
         plan = {"splits": 1, "waves": 8, "workgroups": -(-w.Nq // 256) * w.B * w.H,
                 "workspace_bytes": 16 * -(-w.Nq // 32), "block_causal": True}
-    elif w.kind == "na3d":  # a wave = 2 rows y x 16 positions on X, 4 waves per workgroup
+    elif w.kind == "na3d":  # four waves per workgroup, query tile chosen by the library
         T, Y, X = w.grid
-        plan = {"splits": 1, "waves": 4, "workgroups": w.B * T * -(-Y // 8) * -(-X // 16) * w.H,
+        na = attn.attn_na3d_plan(w.B, T, Y, X, w.H, w.D, *w.kernel)
+        plan = {"splits": 1, "waves": 4, "workgroups": na["workgroups"],
+                "query_tile": [32 // na["query_cols"], na["query_cols"]],
                 "workspace_bytes": 0, "na3d": True}
     else:
         plan = attn.attn_plan(w.B, w.Nq, w.keys, w.H, w.D)
@@ -218,7 +220,7 @@ def kernel_name(D, plan):
     if plan.get("block_causal"):
         return f"attn_bc_meta_kernel + attn_fwd_pp_kernel<{D}, true>"
     if plan.get("na3d"):
-        return "attn_na3d_kernel"
+        return f"attn_na3d_kernel<{plan['query_tile'][1]}>"
     main = (f"attn_fwd_pp_kernel<{D}, false>" if waves == 8 else
             f"attn_fwd_kernel<{D}, {waves}, {32 if D == 128 else 64}>")
     return main if plan["splits"] == 1 else main + f" + attn_combine_kernel<{D}>"

@@ -140,6 +140,17 @@ int attn_plan(int B, int Nq, int Nk, int H, int D, int num_splits, int waves, in
               int* waves_out, long long* workgroups, long long* workspace_bytes);
 
 /*
+ * Launch plan of attn_na3d for these sizes and window, computed on the host only (no
+ * HIP call). Any output pointer may be NULL. Returns ATTN_OK or the size/window error
+ * attn_na3d would return.
+ *   query_cols: positions on X of a wavefront's query tile (16, 8 or 4; the tile is
+ *               32 / query_cols rows y by query_cols positions), chosen per window
+ *   workgroups: workgroups of the kernel
+ */
+int attn_na3d_plan(int B, int T, int Y, int X, int H, int D, int kt, int ky, int kx,
+                   int* query_cols, long long* workgroups);
+
+/*
  * Makes sure the current device's split-KV work space holds at least `bytes`
  * (allocating and synchronising the device if it must grow). Returns ATTN_OK,
  * ATTN_ERR_WORKSPACE or ATTN_ERR_HIP.

@@ -182,3 +182,32 @@ def test_python_na3d_validates_before_the_library():
         attn.na3d(x, x, x, (1, 1, 1))  # CPU tensors are rejected
     with pytest.raises((ValueError, TypeError)):
         attn.na3d(x[0], x[0], x[0], (1, 1, 1))
+
+
+@pytest.mark.parametrize("window,cols", [((3, 7, 7), 8), ((3, 5, 5), 8), ((11, 11, 11), 4),
+                                         ((1, 1, 17), 16), ((1, 3, 13), 16), ((1, 7, 13), 4),
+                                         ((1, 1, 15), 16),
+                                         ((1, 9, 9), 8)])
+def test_na3d_plan_picks_a_tile_that_holds_the_window(window, cols):
+    """A wave's query tile is 32 / c rows by c positions; its key blocks hold 32 positions
+    of one row (c = 16) or 16 positions of two rows (c = 8, 4), so the X windows of the c
+    positions, c - 1 + kx positions wide, must fit; among those the fewest keys per query
+    and t' ((32 / c + ky - 1) rows of the block width) wins."""
+    kt, ky, kx = window
+    B, T, Y, X, H = 2, 11, 37, 45, 3
+    plan = attn.attn_na3d_plan(B, T, Y, X, H, 64, kt, ky, kx)
+    c = plan["query_cols"]
+    assert c == cols
+    width = 32 if c == 16 else 16
+    assert c - 1 + kx <= width
+    rows = 32 // c
+    assert plan["workgroups"] == B * T * -(-Y // (4 * rows)) * -(-X // c) * H
+
+
+def test_na3d_plan_errors_match_the_call():
+    assert attn.attn_na3d_plan(1, 4, 8, 40, 4, 64, 3, 5, 7)["workgroups"] > 0
+    for args, code in [((1, 4, 8, 40, 4, 64, 2, 5, 7), -2), ((1, 4, 8, 40, 4, 128, 3, 5, 7), -3),
+                       ((1, 4, 8, 64, 4, 64, 3, 5, 19), -3), ((1, 4, 8, 1 << 16, 1 << 10, 64, 3, 5, 3), -6)]:
+        with pytest.raises(attn.AttnError) as e:
+            attn.attn_na3d_plan(*args)
+        assert e.value.code == code

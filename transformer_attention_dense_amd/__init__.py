@@ -6,8 +6,8 @@ library is missing or fails to load, importing the low-level functions raises.
 
 Low-level functions (same names and arguments as the C ABI; tensors passed as raw
 device addresses, ``stream`` as an integer hipStream_t):
-    attn_dense, attn_prefix, attn_cross, attn_fwd_ex, attn_plan,
-    attn_reserve_workspace, attn_strerror, attn_abi_version
+    attn_dense, attn_prefix, attn_cross, attn_block_causal, attn_na3d, attn_fwd_ex,
+    attn_plan, attn_na3d_plan, attn_reserve_workspace, attn_strerror, attn_abi_version
 
 Tensor-level helpers (torch is used for device memory and the current stream):
     dense(q, k, v, out=None), prefix(q, kp, vp, kc, vc, out=None),
@@ -37,7 +37,7 @@ ERRORS = {
 # Exported symbols, in header order.
 SYMBOLS = ("attn_dense", "attn_prefix", "attn_cross", "attn_block_causal", "attn_na3d",
            "attn_fwd_ex",
-           "attn_plan", "attn_reserve_workspace", "attn_strerror", "attn_abi_version")
+           "attn_plan", "attn_na3d_plan", "attn_reserve_workspace", "attn_strerror", "attn_abi_version")
 
 
 class AttnError(RuntimeError):
@@ -67,6 +67,7 @@ def library() -> ctypes.CDLL:
     lib.attn_fwd_ex.argtypes = [p, p, p, i, p, p, i, p, i, i, i, i, i, i, p]
     lib.attn_plan.argtypes = [i, i, i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i),
                               ctypes.POINTER(ll), ctypes.POINTER(ll)]
+    lib.attn_na3d_plan.argtypes = [i] * 9 + [ctypes.POINTER(i), ctypes.POINTER(ll)]
     lib.attn_reserve_workspace.argtypes = [ll]
     lib.attn_strerror.argtypes = [i]
     lib.attn_strerror.restype = ctypes.c_char_p
@@ -104,6 +105,16 @@ def attn_fwd_ex(q, k0, v0, n0, k1, v1, n1, out, B, Nq, H, D, num_splits=0, waves
                 stream=0) -> int:
     return library().attn_fwd_ex(q, k0, v0, n0, k1, v1, n1, out, B, Nq, H, D, num_splits,
                                  waves, stream)
+
+
+def attn_na3d_plan(B, T, Y, X, H, D, kt, ky, kx):
+    """Host-only launch plan of attn_na3d: dict(query_cols, workgroups)."""
+    qc, wg = ctypes.c_int(), ctypes.c_longlong()
+    rc = library().attn_na3d_plan(B, T, Y, X, H, D, kt, ky, kx, ctypes.byref(qc),
+                                  ctypes.byref(wg))
+    if rc != ATTN_OK:
+        raise AttnError(rc, "attn_na3d_plan")
+    return {"query_cols": qc.value, "workgroups": wg.value}
 
 
 def attn_plan(B, Nq, Nk, H, D, num_splits=0, waves=0):

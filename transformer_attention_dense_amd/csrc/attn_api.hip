@@ -251,29 +251,15 @@ int run_block_causal(const void* q, const void* k, const void* v, const int* ids
 }
 
 // 3-D neighborhood attention (attn_na3d.hip).
-int run_na3d(const void* q, const void* k, const void* v, void* out, int B, int T, int Y, int X,
-             int H, int D, int kt, int ky, int kx, void* stream) {
-    if (!q || !k || !v || !out) return ATTN_ERR_NULL;
+// Checks the sizes and window of a 3-D neighborhood call and fills p's sizes and launch
+// shape (not its pointers).
+int na3d_shape(int B, int T, int Y, int X, int H, int D, int kt, int ky, int kx,
+               attn::NaParams& p) {
     if (B < 1 || T < 1 || Y < 1 || X < 1 || H < 1) return ATTN_ERR_SHAPE;
     if (kt < 1 || ky < 1 || kx < 1 || kt % 2 == 0 || ky % 2 == 0 || kx % 2 == 0 || kt > T ||
         ky > Y || kx > X)
         return ATTN_ERR_SHAPE;
     if (D != 64 || kx > 17) return ATTN_ERR_UNSUPPORTED;
-    const long long elems = (long long)B * T * Y * X * H * D;
-    // element offsets of whole rows fit in 32 bits per (b, t, y) row of X positions
-    if (elems >= (1LL << 40) || 2LL * X * H * D >= (1LL << 31) ||
-        (long long)B * T * ((Y + 7) / 8) * ((X + 15) / 16) * H >= (1LL << 31))
-        return ATTN_ERR_OVERFLOW;
-    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out)) return ATTN_ERR_ALIGN;
-    const long long bytes = 2 * elems;
-    if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) ||
-        overlaps(out, bytes, v, bytes))
-        return ATTN_ERR_ALIAS;
-    attn::NaParams p;
-    p.q = static_cast<const uint16_t*>(q);
-    p.k = static_cast<const uint16_t*>(k);
-    p.v = static_cast<const uint16_t*>(v);
-    p.out = static_cast<uint16_t*>(out);
     p.B = B;
     p.T = T;
     p.Y = Y;
@@ -282,8 +268,30 @@ int run_na3d(const void* q, const void* k, const void* v, void* out, int B, int 
     p.kt = kt;
     p.ky = ky;
     p.kx = kx;
-    p.strips = (X + 15) / 16;
-    p.yblocks = (Y + 7) / 8;
+    attn::na3d_configure(p);
+    const long long elems = (long long)B * T * Y * X * H * D;
+    // byte offsets within two consecutive (b, t, y) rows of X positions fit in 32 bits
+    if (elems >= (1LL << 40) || 2LL * X * H * D >= (1LL << 31) ||
+        attn::na3d_workgroups(p) >= (1LL << 31))
+        return ATTN_ERR_OVERFLOW;
+    return ATTN_OK;
+}
+
+int run_na3d(const void* q, const void* k, const void* v, void* out, int B, int T, int Y, int X,
+             int H, int D, int kt, int ky, int kx, void* stream) {
+    if (!q || !k || !v || !out) return ATTN_ERR_NULL;
+    attn::NaParams p;
+    const int rc = na3d_shape(B, T, Y, X, H, D, kt, ky, kx, p);
+    if (rc != ATTN_OK) return rc;
+    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out)) return ATTN_ERR_ALIGN;
+    const long long bytes = 2LL * B * T * Y * X * H * D;
+    if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) ||
+        overlaps(out, bytes, v, bytes))
+        return ATTN_ERR_ALIAS;
+    p.q = static_cast<const uint16_t*>(q);
+    p.k = static_cast<const uint16_t*>(k);
+    p.v = static_cast<const uint16_t*>(v);
+    p.out = static_cast<uint16_t*>(out);
     if (attn::launch_na3d(p, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
         return ATTN_ERR_HIP;
     return ATTN_OK;
@@ -338,6 +346,16 @@ int attn_plan(int B, int Nq, int Nk, int H, int D, int num_splits, int waves, in
     if (waves_out) *waves_out = plan.waves;
     if (workgroups) *workgroups = plan.workgroups;
     if (workspace_bytes) *workspace_bytes = plan.workspace_bytes;
+    return ATTN_OK;
+}
+
+int attn_na3d_plan(int B, int T, int Y, int X, int H, int D, int kt, int ky, int kx,
+                   int* query_cols, long long* workgroups) {
+    attn::NaParams p;
+    const int rc = na3d_shape(B, T, Y, X, H, D, kt, ky, kx, p);
+    if (rc != ATTN_OK) return rc;
+    if (query_cols) *query_cols = p.qb;
+    if (workgroups) *workgroups = attn::na3d_workgroups(p);
     return ATTN_OK;
 }
 

@@ -51,9 +51,12 @@ struct NaParams {
     uint16_t* out;
     int B, T, Y, X, H;
     int kt, ky, kx;
-    int strips;   // ceil(X / 16): strips of 16 positions on the X axis
-    int yblocks;  // ceil(Y / 8): eight query rows y per workgroup
+    // set by na3d_configure: a wave's query tile (32 / qb rows y x qb positions on X)
+    int qb;       // 16, 8 or 4
+    int strips;   // ceil(X / qb): strips of qb positions on the X axis
+    int yblocks;  // ceil(Y / (4 * 32 / qb)): blocks of rows y of a workgroup
 };
+void na3d_configure(NaParams& p);
 long long na3d_workgroups(const NaParams& p);
 hipError_t launch_na3d(const NaParams& p, hipStream_t stream);
 

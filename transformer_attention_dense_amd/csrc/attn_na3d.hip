@@ -5,22 +5,22 @@
 // neighborhood is NATTEN's: on each axis an odd window centred on the query, moved
 // inside the axis at its ends).
 //
-// A wave owns 32 queries: 16 consecutive positions on the X axis in two consecutive
-// rows y, at one (b, t, h); a workgroup stacks four waves on Y (8 rows). Every (t', y')
-// row of a query's window is a run of consecutive positions on X, and the X windows of
-// the 16 positions lie in the 32 positions starting at the window of the first one (a
-// window is at most 17 wide), so one 32-key tile per row holds them all. The workgroup
-// walks the union of its eight rows' Y windows (ky + 7 rows for interior blocks) for
-// each t' of the common T window, as 32-key tiles streamed through a four-slot LDS
-// ring exactly like the dense kernels stream key tiles; each tile is copied once and
-// used by every wave whose rows' windows contain its row:
+// A wave owns 32 queries of one (b, t, h): QA rows y x QB positions on X (QB = 16, 8 or
+// 4, QA = 32 / QB, picked per window shape); a workgroup stacks four waves on Y. Every
+// (t', y') row of a query's window is a run of consecutive positions on X, and the X
+// windows of the QB positions lie in the KW positions starting at the window of the first
+// one (KW = 32 for QB = 16, else 16; kx <= KW - QB + 1), so a key block of 32 keys holds
+// KW positions of 32 / KW rows. The workgroup walks the union of its rows' Y windows for
+// each t' of the common T window as such blocks, streamed through a four-slot LDS ring
+// exactly like the dense kernels stream key tiles; each block is copied once and used by
+// every wave whose rows' windows reach its rows:
 //
-//   * copy the K and V tile of the row (global_load_lds_dwordx4, scalar base +
-//     per-lane offsets fixed for the workgroup; positions past the end of the X axis
-//     are clamped and never visible), three tiles ahead of their use;
+//   * copy the K and V block (global_load_lds_dwordx4, scalar base + per-lane offsets
+//     fixed for the workgroup; positions past the end of the X axis are clamped and never
+//     visible), three blocks ahead of their use;
 //   * S^T = K Q^T with 32x32x16 BF16 MFMAs (S in FP32); per lane, keys outside its
-//     query's X window, and the whole tile when its row is outside the query's Y window,
-//     get -inf added;
+//     query's X window get -inf added, and keys of rows outside its Y window too where
+//     the block is not inside every Y window of the wave;
 //   * online softmax in the exp2 domain (scale 1, so c = log2 e), P rounded to BF16;
 //   * O^T += V^T P^T with the V operand read transposed from LDS (ds_read_b64_tr_b16).
 #include <hip/hip_runtime.h>
@@ -54,26 +54,39 @@ __device__ __forceinline__ void barrier_tiles_left(int left) {
 }
 
 constexpr int kNaWaves = 4;  // waves per workgroup, stacked on Y
-constexpr int kNaRows = 2;   // rows y per wave
-constexpr int kNaXs = 16;    // positions on X per wave
+
+// Query tile of a wave: QA rows y x QB positions on X (32 queries). A key block is RPB
+// rows of KW positions on X (32 keys), the X windows of the QB positions lying in the KW
+// positions from the window of the first one (so kx <= KW - QB + 1).
+template <int QB>
+struct NaTile {
+    static constexpr int QA = 32 / QB;
+    static constexpr int KW = QB == 16 ? 32 : 16;
+    static constexpr int RPB = 32 / KW;
+    static constexpr int max_kx = KW - QB + 1;
+};
 
 // Four waves per SIMD (at most 128 VGPRs): the kernel is latency bound, and above 128
 // registers the compiler keeps the MFMA accumulators in AGPRs and copies them around.
+template <int QB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
 void attn_na3d_kernel(NaParams p) {
+    using Tile = NaTile<QB>;
+    constexpr int QA = Tile::QA, KW = Tile::KW, RPB = Tile::RPB;
     constexpr int D = 64;
     constexpr int KS = D / 16;       // MFMA k-steps over the head dim
     constexpr int DB = D / 32;       // 32-wide head-dim blocks of O^T
     constexpr int CPR = D / 8;       // 16-byte chunks per row
     constexpr int ROWB = 2 * D;      // bytes per LDS row
-    constexpr int BN = 32;           // keys per tile
-    constexpr int TILEB = BN * ROWB; // bytes per K or V tile
+    constexpr int BN = 32;           // keys per block
+    constexpr int TILEB = BN * ROWB; // bytes per K or V block
     constexpr int NT = kNaWaves * kWave;
-    static_assert(BN * CPR == NT, "one 16-byte copy per thread per tensor and tile");
+    static_assert(BN * CPR == NT, "one 16-byte copy per thread per tensor and block");
     constexpr int NSLOT = 4;         // LDS ring slots
-    constexpr int AHEAD = NSLOT - 1; // tiles copied ahead of the one in use
-    constexpr int NPAIR = 8;         // exp pairs per lane per tile
-    constexpr int YB = kNaWaves * kNaRows;  // rows y per workgroup
+    constexpr int AHEAD = NSLOT - 1; // blocks copied ahead of the one in use
+    constexpr int NPAIR = 8;         // exp pairs per lane per block
+    constexpr int YB = kNaWaves * QA;  // rows y per workgroup
+    constexpr int NXM = KW == 16 ? 8 : 16;  // distinct X masks per lane
 
     __shared__ __attribute__((aligned(1024))) char smem[NSLOT * 2 * TILEB];
 
@@ -83,7 +96,7 @@ void attn_na3d_kernel(NaParams p) {
     const int n = lane & 31;
     const int g = lane >> 5;
 
-    // workgroup -> (b, t, block of eight rows y, strip of 16 on X, h), h fastest
+    // workgroup -> (b, t, block of YB rows y, strip of QB positions on X, h), h fastest
     long idx = blockIdx.x;
     const int h = (int)(idx % p.H);
     idx /= p.H;
@@ -96,10 +109,10 @@ void attn_na3d_kernel(NaParams p) {
 
     const int X = p.X, Y = p.Y;
     const long HD = (long)p.H * D;
-    const int wy0 = yblk * YB + wave * kNaRows;  // the wave's first row y
+    const int wy0 = yblk * YB + wave * QA;  // the wave's first row y
     const bool active = wy0 < Y;
-    const int yq = wy0 + (n >> 4);               // this lane's query row
-    const int xq = strip * kNaXs + (n & 15);     // and position on X
+    const int yq = wy0 + n / QB;            // this lane's query row
+    const int xq = strip * QB + n % QB;     // and position on X
     const bool qvalid = yq < Y && xq < X;
     const int yqc = min(yq, Y - 1), xqc = min(xq, X - 1);
     const long pos_q = (((long)b * p.T + t) * Y + yqc) * X + xqc;
@@ -117,35 +130,42 @@ void attn_na3d_kernel(NaParams p) {
     const int t0 = na_start(t, p.kt, p.T);
     const int ys_q = na_start(yqc, p.ky, Y);
     const int xs_q = na_start(xqc, p.kx, X);
-    const int xa = na_start(strip * kNaXs, p.kx, X);  // first key position of a tile
-    // rows y' the wave needs (its two rows' windows) and the workgroup walks (eight)
+    const int xa = na_start(strip * QB, p.kx, X);  // first key position of a block
+    // rows y' the wave needs (the union of its rows' windows), the rows every one of
+    // its queries sees (the intersection), and the rows the workgroup walks
+    const int wlast = min(wy0 + QA - 1, Y - 1);
     const int wv0 = na_start(min(wy0, Y - 1), p.ky, Y);
-    const int wv1 = na_start(min(wy0 + kNaRows - 1, Y - 1), p.ky, Y) + p.ky;
+    const int wv1 = na_start(wlast, p.ky, Y) + p.ky;
+    const int wc0 = na_start(wlast, p.ky, Y);
+    const int wc1 = wv0 + p.ky;
     const int yu0 = na_start(min(yblk * YB, Y - 1), p.ky, Y);
     const int yu1 = na_start(min(yblk * YB + YB - 1, Y - 1), p.ky, Y) + p.ky;
-    const int nyu = yu1 - yu0;
-    const int ntiles = p.kt * nyu;
+    const int nbr = (yu1 - yu0 + RPB - 1) / RPB;  // blocks per t'
+    const int nblocks = p.kt * nbr;
 
-    // Loader: thread tid copies physical chunk tid of a tile: row r = tid / CPR,
-    // position tid % CPR holding logical chunk (tid % CPR) ^ swizzle(r); the source
-    // position xa + r is clamped to the axis.
-    unsigned ld_off;
+    // Loader: thread tid copies physical chunk tid of a block: key j = tid / CPR (row
+    // j / KW of the block, position xa + j % KW, clamped to the axis), position tid % CPR
+    // holding logical chunk (tid % CPR) ^ swizzle(j). ld_off1 reads the block's first row
+    // in place of its second, for a last block whose second row is past the axis.
+    unsigned ld_off, ld_off1;
     {
-        const int r = tid / CPR;
-        const int xk = min(xa + r, X - 1);
-        const int chunk = (tid % CPR) ^ lds_swizzle<CPR>(r);
-        ld_off = (unsigned)(2 * ((long)xk * HD + chunk * 8));
+        const int j = tid / CPR;
+        const int xk = min(xa + j % KW, X - 1);
+        const int chunk = (tid % CPR) ^ lds_swizzle<CPR>(j);
+        ld_off1 = (unsigned)(2 * ((long)xk * HD + chunk * 8));
+        ld_off = ld_off1 + (unsigned)(2 * (long)(j / KW) * X * HD);
     }
     const char* kbase = reinterpret_cast<const char*>(uniform_ptr(p.k));
     const char* vbase = reinterpret_cast<const char*>(uniform_ptr(p.v));
     auto kslot = [&](int j) { return smem + j * 2 * TILEB; };
     auto vslot = [&](int j) { return smem + j * 2 * TILEB + TILEB; };
-    // tile i: row (t0 + i / nyu, yu0 + i % nyu) into slot i % NSLOT
-    auto issue_tile = [&](int i) {
-        const int tt = t0 + i / nyu, yy = yu0 + i % nyu;
+    // block i: rows (t0 + i / nbr, yu0 + RPB * (i % nbr) ...) into slot i % NSLOT
+    auto issue_block = [&](int i) {
+        const int tt = t0 + i / nbr, yy = yu0 + RPB * (i % nbr);
         const long rb = ((((long)b * p.T + tt) * Y + yy) * X * HD + (long)h * D) * 2;
-        load16_to_lds_sbase(kbase + rb, ld_off, kslot(i % NSLOT) + wave * kWave * 16);
-        load16_to_lds_sbase(vbase + rb, ld_off, vslot(i % NSLOT) + wave * kWave * 16);
+        const unsigned off = (RPB == 1 || yy + 1 < Y) ? ld_off : ld_off1;
+        load16_to_lds_sbase(kbase + rb, off, kslot(i % NSLOT) + wave * kWave * 16);
+        load16_to_lds_sbase(vbase + rb, off, vslot(i % NSLOT) + wave * kWave * 16);
     };
 
     // Per-lane LDS byte offsets: K operand reads per k-step, V transpose reads per
@@ -175,19 +195,24 @@ void attn_na3d_kernel(NaParams p) {
 #pragma unroll
     for (int i = 0; i < DB; ++i) o[i] = f32x16{};
     float m_ref = -INFINITY;
-    float l_part = 0.f;
+    float l_part = 0.f;  // this lane's partial row sum (of BF16-rounded probabilities)
     const float c = 1.4426950408889634f;  // log2(e): scale 1
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-    // The X window of a query covers the same keys of every tile (the tiles share
-    // their X positions): keys outside it get -inf added, one add per score.
-    f32x16 xmask;
+    // Score register r of a lane holds key j = 8 (r / 4) + 4 g + r % 4 of the block: row
+    // j / KW, position xa + j % KW. The X window of a query covers the same keys of every
+    // block: keys outside it get -inf added (registers r and r + 8 share a position when
+    // KW = 16).
+    float xm[NXM];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int xk = xa + 8 * (r >> 2) + 4 * g + (r & 3);
-        xmask[r] = (xk < xs_q || xk >= xs_q + p.kx) ? -INFINITY : 0.f;
+    for (int r = 0; r < NXM; ++r) {
+        const int xk = xa + (8 * (r >> 2) + 4 * g + (r & 3)) % KW;
+        xm[r] = (xk < xs_q || xk >= xs_q + p.kx) ? -INFINITY : 0.f;
     }
 
-    auto compute = [&](const char* kt_lds, const char* vt_lds, int yy) {
+    // One block; ymask when some of its rows lie outside the Y window of some query of
+    // the wave (those rows' keys get -inf for that query). ymask is uniform.
+    auto compute = [&](const char* kt_lds, const char* vt_lds, int yy, bool ymask) {
         // ---- S^T = K Q^T
         f32x16 s = f32x16{};
 #pragma unroll
@@ -195,11 +220,18 @@ void attn_na3d_kernel(NaParams p) {
             const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt_lds + koff[ks]);
             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s, 0, 0, 0);
         }
-        // ---- keys outside the query's window are hidden (a row outside its Y window
-        // hides the whole tile for that query)
-        const float ymask = (yy >= ys_q && yy < ys_q + p.ky) ? 0.f : -INFINITY;
-        s += xmask + ymask;
-        // ---- online softmax: running maximum raised only when a row's tile maximum
+        // ---- keys outside the query's window are hidden
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] += xm[r % NXM];
+        if (ymask) {
+#pragma unroll
+            for (int hr = 0; hr < RPB; ++hr) {
+                const float ym = (yy + hr >= ys_q && yy + hr < ys_q + p.ky) ? 0.f : -INFINITY;
+#pragma unroll
+                for (int r = 8 * hr; r < (RPB == 2 ? 8 * hr + 8 : 16); ++r) s[r] += ym;
+            }
+        }
+        // ---- online softmax: running maximum raised only when a row's block maximum
         // exceeds it by more than 2^kRescaleLog2 in the exp2 domain
         float mx = s[0];
 #pragma unroll
@@ -223,7 +255,7 @@ void attn_na3d_kernel(NaParams p) {
             const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -mc));
             const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 1], c, -mc));
             const bf16x2 pk = {(__bf16)e0, (__bf16)e1};
-            l_part += e0 + e1;
+            l_part = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, l_part, false);
             pf[tt2][r & 7] = pk[0];
             pf[tt2][(r & 7) + 1] = pk[1];
         });
@@ -242,16 +274,16 @@ void attn_na3d_kernel(NaParams p) {
         }
     };
 
-    // ---- pipeline: tile i is copied AHEAD tiles ahead into slot i % NSLOT; the
-    // barrier before tile i waits for its copies and lets the later ones stay in flight
-    const int npre = min(AHEAD, ntiles);
-    for (int i = 0; i < npre; ++i) issue_tile(i);
-    for (int i = 0; i < ntiles; ++i) {
-        barrier_tiles_left<AHEAD - 1>(ntiles - 1 - i);
-        if (i + AHEAD < ntiles) issue_tile(i + AHEAD);  // into the slot tile i-1 left
-        const int yy = yu0 + i % nyu;
-        if (active && yy >= wv0 && yy < wv1)
-            compute(kslot(i % NSLOT), vslot(i % NSLOT), yy);
+    // ---- pipeline: block i is copied AHEAD blocks ahead into slot i % NSLOT; the
+    // barrier before block i waits for its copies and lets the later ones stay in flight
+    const int npre = min(AHEAD, nblocks);
+    for (int i = 0; i < npre; ++i) issue_block(i);
+    for (int i = 0; i < nblocks; ++i) {
+        barrier_tiles_left<AHEAD - 1>(nblocks - 1 - i);
+        if (i + AHEAD < nblocks) issue_block(i + AHEAD);  // into the slot block i-1 left
+        const int yy = yu0 + RPB * (i % nbr);
+        if (active && yy < wv1 && yy + RPB > wv0)
+            compute(kslot(i % NSLOT), vslot(i % NSLOT), yy, yy < wc0 || yy + RPB > wc1);
     }
 
     // ---- epilogue
@@ -273,13 +305,40 @@ void attn_na3d_kernel(NaParams p) {
 
 }  // namespace
 
+// Picks the wave tile whose key blocks cover a query's window with the fewest keys per
+// t' ((QA + ky - 1) rows of KW positions), among those whose blocks hold the X windows.
+void na3d_configure(NaParams& p) {
+    struct Opt { int qb, qa, kw, max_kx; };
+    const Opt opts[] = {{16, NaTile<16>::QA, NaTile<16>::KW, NaTile<16>::max_kx},
+                        {8, NaTile<8>::QA, NaTile<8>::KW, NaTile<8>::max_kx},
+                        {4, NaTile<4>::QA, NaTile<4>::KW, NaTile<4>::max_kx}};
+    long best = -1;
+    p.qb = 0;
+    p.strips = p.yblocks = 0;  // no tile holds the window: nothing to launch
+    for (const Opt& o : opts) {
+        if (p.kx > o.max_kx) continue;
+        const long cost = (long)(o.qa + p.ky - 1) * o.kw;
+        if (best < 0 || cost < best) {
+            best = cost;
+            p.qb = o.qb;
+            p.strips = (p.X + o.qb - 1) / o.qb;
+            p.yblocks = (p.Y + kNaWaves * o.qa - 1) / (kNaWaves * o.qa);
+        }
+    }
+}
+
 long long na3d_workgroups(const NaParams& p) {
     return (long long)p.B * p.T * p.yblocks * p.strips * p.H;
 }
 
 hipError_t launch_na3d(const NaParams& p, hipStream_t stream) {
-    hipLaunchKernelGGL(attn_na3d_kernel, dim3((unsigned)na3d_workgroups(p)), dim3(256), 0,
-                       stream, p);
+    const dim3 grid((unsigned)na3d_workgroups(p)), block(kNaWaves * kWave);
+    switch (p.qb) {
+        case 16: hipLaunchKernelGGL(attn_na3d_kernel<16>, grid, block, 0, stream, p); break;
+        case 8: hipLaunchKernelGGL(attn_na3d_kernel<8>, grid, block, 0, stream, p); break;
+        case 4: hipLaunchKernelGGL(attn_na3d_kernel<4>, grid, block, 0, stream, p); break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
