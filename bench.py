@@ -22,6 +22,10 @@ Options beyond the common ones:
   --ingest F W      read two rocprofv3 --pmc CSVs (FETCH_SIZE run, WRITE_SIZE run) of a
                     --calib-mib run and write profiles/traffic.json (HBM bytes per launch
                     of the attention kernel, scaled by the calibration)
+  --ingest-mfma DIR read the output directory of one rocprofv3 --kernel-trace --pmc run with
+                    GRBM_GUI_ACTIVE, SQ_VALU_MFMA_BUSY_CYCLES and SQ_INSTS_VALU_MFMA_MOPS_BF16
+                    and add, to the same file, the attention kernel's MFMA utilisation and
+                    its shader clock while it ran
 """
 import argparse
 import hashlib
@@ -66,6 +70,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calib-mib", type=int, default=0)
     ap.add_argument("--ingest", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--ingest-mfma", metavar="PMC_DIR")
     return ap.parse_args()
 
 
@@ -91,17 +96,23 @@ def make_call(w, dts, attn):
     return out, (lambda: attn.prefix(*dts, out=out))
 
 
-def traffic_for(w):
-    """HBM bytes per launch from committed counter runs, if taken on this kernel source."""
+def counters_for(w):
+    """The committed counter readings of this workload (HBM bytes per launch, MFMA
+    utilisation, shader clock), if they were taken on the current kernel sources."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
-        return None
+        return {}
     entry = t.get("workloads", {}).get(w.name)
     if not entry or entry.get("kernel_source_hash") != kernel_source_hash(w.kind):
-        return None
-    return entry.get("hbm_bytes_per_launch")
+        return {}
+    return entry
+
+
+def traffic_for(w):
+    """HBM bytes per launch from committed counter runs, if taken on this kernel source."""
+    return counters_for(w).get("hbm_bytes_per_launch")
 
 
 def cpu_baseline(w, seconds):
@@ -221,8 +232,11 @@ def kernel_name(D, plan):
         return f"attn_bc_meta_kernel + attn_fwd_pp_kernel<{D}, true>"
     if plan.get("na3d"):
         return f"attn_na3d_kernel<{plan['query_tile'][1]}>"
+    # attn_fwd_kernel<D, waves, keys per tile, LDS slots>, as the library instantiates it
+    bn = 32 if (D == 128 and waves == 2) else 64
+    nslot = 2 if (D == 128 and waves == 4) else 3
     main = (f"attn_fwd_pp_kernel<{D}, false>" if waves == 8 else
-            f"attn_fwd_kernel<{D}, {waves}, {32 if D == 128 else 64}>")
+            f"attn_fwd_kernel<{D}, {waves}, {bn}, {nslot}>")
     return main if plan["splits"] == 1 else main + f" + attn_combine_kernel<{D}>"
 
 
@@ -272,6 +286,13 @@ def record(w, r, steps, warmup, cpu):
                                 "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                 "frac": round(rec["roofline"]["hbm_gbs_algorithmic"]
                                               / PEAK_HBM_GBS, 4)})
+    mf = counters_for(w).get("mfma")
+    if mf and rec["roofline"]["bound"] == "mfma" and mf["profiled_duration_us"] >= 100:
+        # From a separate counter run of the same kernel source (counters perturb timing).
+        # GRBM_GUI_ACTIVE also counts some 13-16 thousand cycles per dispatch outside the
+        # kernel's own time stamps, so these read a few percent off for long kernels and
+        # mean nothing for short ones, which are left out.
+        rec["roofline"].update({"mfma_util": mf["mfma_util"], "clock_ghz": mf["clock_ghz"]})
     if w.kind == "na3d":
         rec["config"].update({"grid": list(w.grid), "kernel": list(w.kernel)})
     if cpu is not None:
@@ -301,36 +322,111 @@ def _counter_means(csv_path, counter):
 def ingest(fetch_csv, write_csv, calib_mib, workload_name):
     """FETCH_SIZE and WRITE_SIZE are in KiB per dispatch; each is scaled by what the same
     counter reads for the calibration kernel, which moves exactly calib_mib MiB each way."""
-    import synth
     known = calib_mib * 1024.0  # KiB
     fa, fc = _counter_means(fetch_csv, "FETCH_SIZE")
     wa, wc = _counter_means(write_csv, "WRITE_SIZE")
     ff, wf = known / fc, known / wc
     hbm = (fa * ff + wa * wf) * 1024.0
+    entry = _update_entry(workload_name, {
+        "hbm_bytes_per_launch": round(hbm),
+        "fetch_kib_raw": fa, "write_kib_raw": wa,
+        "calibration": {"kib_each_way": known, "fetch_kib_read": fc, "write_kib_read": wc,
+                        "fetch_factor": ff, "write_factor": wf},
+    })
+    print(json.dumps(entry))
+
+
+def _update_entry(workload_name, fields):
+    """Merges fields into the workload's entry of the counter file; an entry taken on
+    other kernel sources is dropped first."""
+    import synth
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         t = {}
     t.pop("kernel_source_hash", None)
-    t.setdefault("workloads", {})[workload_name] = {
-        "kernel_source_hash": kernel_source_hash(synth.workload(workload_name).kind),
-        "hbm_bytes_per_launch": round(hbm),
-        "fetch_kib_raw": fa, "write_kib_raw": wa,
-        "calibration": {"kib_each_way": known, "fetch_kib_read": fc, "write_kib_read": wc,
-                        "fetch_factor": ff, "write_factor": wf},
-    }
+    h = kernel_source_hash(synth.workload(workload_name).kind)
+    ws = t.setdefault("workloads", {})
+    entry = ws.get(workload_name, {})
+    if entry.get("kernel_source_hash") != h:
+        entry = {}
+    entry.update(fields)
+    entry["kernel_source_hash"] = h
+    ws[workload_name] = entry
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(t, f, indent=1, sort_keys=True)
         f.write("\n")
-    print(json.dumps(t["workloads"][workload_name]))
+    return entry
+
+
+def ingest_mfma(pmc_dir, workload_name):
+    """MFMA utilisation and shader clock of the attention kernel from one rocprofv3
+    --kernel-trace --pmc run (the last dispatches, i.e. the timed ones).
+
+    GRBM_GUI_ACTIVE reads the busy cycles of all XCDs added together, so cycles per
+    XCD = GRBM_GUI_ACTIVE / Num_Xcc, and the clock = that / the dispatch's duration.
+    SQ_VALU_MFMA_BUSY_CYCLES adds the busy cycles of the matrix units of all SIMDs, so
+    utilisation = SQ_VALU_MFMA_BUSY_CYCLES / (cycles per XCD * Simd_Count).
+    SQ_INSTS_VALU_MFMA_MOPS_BF16 counts BF16 MFMA work in units of 512 FLOP; it is
+    checked against the algorithmic FLOP of a launch."""
+    import csv
+    import glob
+    import synth
+    w = synth.workload(workload_name)
+
+    def one(pattern):
+        found = glob.glob(os.path.join(pmc_dir, "**", pattern), recursive=True)
+        if len(found) != 1:
+            raise SystemExit(f"{pmc_dir}: expected one {pattern}, found {found}")
+        with open(found[0]) as f:
+            return list(csv.DictReader(f))
+
+    agent = next(a for a in one("*agent_info.csv") if a.get("Name", "").startswith("gfx"))
+    xcc, simds = int(agent["Num_Xcc"]), int(agent["Simd_Count"])
+
+    def is_main(name):
+        return "attn_fwd" in name or "attn_na3d" in name
+
+    per = {}
+    for r in one("*counter_collection.csv"):
+        if is_main(r["Kernel_Name"]):
+            d = per.setdefault(int(r["Dispatch_Id"]), {})
+            d[r["Counter_Name"]] = float(r["Counter_Value"])
+    dur = {int(r["Dispatch_Id"]): int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+           for r in one("*kernel_trace.csv") if is_main(r["Kernel_Name"])}
+    ids = sorted(i for i in per if i in dur)[-100:]
+    if not ids:
+        raise SystemExit(f"{pmc_dir}: no attention dispatches with counters and durations")
+    cyc = sum(per[i]["GRBM_GUI_ACTIVE"] for i in ids) / len(ids) / xcc
+    busy = sum(per[i]["SQ_VALU_MFMA_BUSY_CYCLES"] for i in ids) / len(ids)
+    mops = sum(per[i]["SQ_INSTS_VALU_MFMA_MOPS_BF16"] for i in ids) / len(ids)
+    ns = sum(dur[i] for i in ids) / len(ids)
+    mf = {"mfma_util": round(busy / (cyc * simds), 4),
+          "clock_ghz": round(cyc / ns, 3),
+          "dispatches": len(ids),
+          "profiled_duration_us": round(ns / 1000.0, 2),
+          "cycles_per_xcd": round(cyc),
+          "mfma_busy_cycles": round(busy),
+          "mfma_flop_counted": round(mops * 512),
+          "algorithmic_flop": w.flop,
+          "max_clock_ghz": float(agent.get("Max_Engine_Clk_Fcompute", 0)) / 1000.0,
+          "peak_at_measured_clock_tflops": round(
+              PEAK_BF16_TFLOPS * (cyc / ns) / (float(agent.get("Max_Engine_Clk_Fcompute", 0))
+                                               / 1000.0), 1)
+          if float(agent.get("Max_Engine_Clk_Fcompute", 0)) > 0 else None}
+    entry = _update_entry(workload_name, {"mfma": mf})
+    print(json.dumps(entry["mfma"]))
 
 
 def main():
     args = parse()
     if args.ingest:
         ingest(args.ingest[0], args.ingest[1], args.calib_mib or 256, args.workload)
+        return
+    if args.ingest_mfma:
+        ingest_mfma(args.ingest_mfma, args.workload)
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
