@@ -332,6 +332,25 @@ def test_na3d_writes_only_its_output():
     assert bool((big[:q.numel()] == 7.0).all()) and bool((big[2 * q.numel():] == 7.0).all())
 
 
+# ---------------------------------------------------------------- streams
+
+def test_calls_run_on_the_current_stream():
+    """The tensor helpers enqueue on the caller's current stream (here a side stream of
+    default priority): the handle they pass is that stream's, and the result equals the
+    same call on the default stream bit for bit."""
+    say("current-stream case: dense B=1 N=130 H=2 D=64 on a side stream")
+    w = synth.small("dense", 1, 130, 2, 64, 905)
+    q, k, v = (dev(t) for t in w.tensors())
+    ref = host(attn.dense(q, k, v))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        assert attn._stream(q) == side.cuda_stream
+        out = attn.dense(q, k, v)
+    side.synchronize()
+    assert np.array_equal(host(out), ref)
+
+
 # ---------------------------------------------------------------- HIP graph capture
 
 def test_graph_capture_replays_match_eager():

@@ -150,8 +150,20 @@ def strerror(code) -> str:
 
 # ---------------------------------------------------------------- tensor helpers
 
+_torch = None
+
+
+def _t():
+    """torch, imported on first use (the low-level functions above do not need it)."""
+    global _torch
+    if _torch is None:
+        import torch
+        _torch = torch
+    return _torch
+
+
 def _check(t, name, shape=None):
-    import torch
+    torch = _t()
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype != torch.bfloat16:
@@ -165,12 +177,18 @@ def _check(t, name, shape=None):
 
 
 def _stream(t):
-    import torch
+    """The current stream of t's device as a raw hipStream_t. torch's raw accessor
+    returns the handle without building a Stream object (a few microseconds per call,
+    which is most of the host cost of a small call); the public path is the fallback."""
+    torch = _t()
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return raw(t.device.index)
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
 def _out(q, out):
-    import torch
+    torch = _t()
     if out is None:
         return torch.empty_like(q)
     _check(out, "out", q.shape)
@@ -232,7 +250,7 @@ def block_causal(q, k, v, image_ids, out=None):
     """Block-causal attention without prefix in the pages' operand order (Q, K_current,
     V_current, image_ids): row i sees key j when j <= i or when both carry the same
     nonnegative image id. image_ids: int32 [N] on the same GPU (text = -1)."""
-    import torch
+    torch = _t()
     _check(q, "q")
     B, N, H, D = q.shape
     _check(k, "k_current", q.shape)
@@ -254,7 +272,7 @@ def na3d(q, k, v, kernel, out=None):
     """3-D neighborhood attention: q, k, v [B, T, Y, X, H, D] bf16 on the GPU, D = 64,
     kernel = (kt, ky, kx) odd window sizes; scores are plain dot products (the model's
     scale is in q)."""
-    import torch
+    torch = _t()
     for t, name in ((q, "q"), (k, "k"), (v, "v")):
         if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16:
             raise TypeError(f"{name} must be a bfloat16 torch.Tensor")
