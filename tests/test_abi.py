@@ -109,9 +109,11 @@ def test_plan_for_the_workloads():
     # D = 64 keeps two 4-wave workgroups per CU
     p2 = attn.attn_plan(2, 16384, 16384, 32, 64)
     assert p2["waves"] == 4 and p2["workgroups"] == 128 * 64
-    # too few 256-row blocks: 4-wave workgroups; short sequences: 2 waves
+    # too few 256-row blocks, and fewer than 256 128-row blocks: 2-wave workgroups
+    # (64 rows each); short sequences: 2 waves
     p0 = attn.attn_plan(1, 256, 256, 32, 64)
-    assert p0["waves"] == 4
+    assert p0["waves"] == 2 and p0["workgroups"] == 4 * 32 and p0["splits"] == 1
+    assert attn.attn_plan(1, 512, 512, 64, 64)["waves"] == 4
     assert attn.attn_plan(1024, 64, 64, 32, 64)["waves"] == 2
     # few query blocks and long keys -> the keys are split and a work space is needed
     ps = attn.attn_plan(1, 64, 8192, 2, 128)
