@@ -361,20 +361,19 @@ def _update_entry(workload_name, fields):
     return entry
 
 
-def ingest_mfma(pmc_dir, workload_name):
-    """MFMA utilisation and shader clock of the attention kernel from one rocprofv3
-    --kernel-trace --pmc run (the last dispatches, i.e. the timed ones).
+def mfma_from_dir(pmc_dir, algorithmic_flop, last=100):
+    """MFMA utilisation and shader clock of the attention kernel from the output
+    directory of one rocprofv3 --kernel-trace --pmc run (its last `last` dispatches, i.e.
+    the timed ones).
 
     GRBM_GUI_ACTIVE reads the busy cycles of all XCDs added together, so cycles per
     XCD = GRBM_GUI_ACTIVE / Num_Xcc, and the clock = that / the dispatch's duration.
     SQ_VALU_MFMA_BUSY_CYCLES adds the busy cycles of the matrix units of all SIMDs, so
     utilisation = SQ_VALU_MFMA_BUSY_CYCLES / (cycles per XCD * Simd_Count).
     SQ_INSTS_VALU_MFMA_MOPS_BF16 counts BF16 MFMA work in units of 512 FLOP; it is
-    checked against the algorithmic FLOP of a launch."""
+    reported beside the algorithmic FLOP of a launch."""
     import csv
     import glob
-    import synth
-    w = synth.workload(workload_name)
 
     def one(pattern):
         found = glob.glob(os.path.join(pmc_dir, "**", pattern), recursive=True)
@@ -385,6 +384,7 @@ def ingest_mfma(pmc_dir, workload_name):
 
     agent = next(a for a in one("*agent_info.csv") if a.get("Name", "").startswith("gfx"))
     xcc, simds = int(agent["Num_Xcc"]), int(agent["Simd_Count"])
+    max_ghz = float(agent.get("Max_Engine_Clk_Fcompute") or 0) / 1000.0
 
     def is_main(name):
         return "attn_fwd" in name or "attn_na3d" in name
@@ -396,26 +396,31 @@ def ingest_mfma(pmc_dir, workload_name):
             d[r["Counter_Name"]] = float(r["Counter_Value"])
     dur = {int(r["Dispatch_Id"]): int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
            for r in one("*kernel_trace.csv") if is_main(r["Kernel_Name"])}
-    ids = sorted(i for i in per if i in dur)[-100:]
+    ids = sorted(i for i in per if i in dur)[-last:]
     if not ids:
         raise SystemExit(f"{pmc_dir}: no attention dispatches with counters and durations")
     cyc = sum(per[i]["GRBM_GUI_ACTIVE"] for i in ids) / len(ids) / xcc
     busy = sum(per[i]["SQ_VALU_MFMA_BUSY_CYCLES"] for i in ids) / len(ids)
     mops = sum(per[i]["SQ_INSTS_VALU_MFMA_MOPS_BF16"] for i in ids) / len(ids)
     ns = sum(dur[i] for i in ids) / len(ids)
-    mf = {"mfma_util": round(busy / (cyc * simds), 4),
-          "clock_ghz": round(cyc / ns, 3),
-          "dispatches": len(ids),
-          "profiled_duration_us": round(ns / 1000.0, 2),
-          "cycles_per_xcd": round(cyc),
-          "mfma_busy_cycles": round(busy),
-          "mfma_flop_counted": round(mops * 512),
-          "algorithmic_flop": w.flop,
-          "max_clock_ghz": float(agent.get("Max_Engine_Clk_Fcompute", 0)) / 1000.0,
-          "peak_at_measured_clock_tflops": round(
-              PEAK_BF16_TFLOPS * (cyc / ns) / (float(agent.get("Max_Engine_Clk_Fcompute", 0))
-                                               / 1000.0), 1)
-          if float(agent.get("Max_Engine_Clk_Fcompute", 0)) > 0 else None}
+    ghz = cyc / ns
+    return {"mfma_util": round(busy / (cyc * simds), 4),
+            "clock_ghz": round(ghz, 3),
+            "dispatches": len(ids),
+            "profiled_duration_us": round(ns / 1000.0, 2),
+            "cycles_per_xcd": round(cyc),
+            "mfma_busy_cycles": round(busy),
+            "mfma_flop_counted": round(mops * 512),
+            "algorithmic_flop": algorithmic_flop,
+            "max_clock_ghz": max_ghz,
+            "peak_at_measured_clock_tflops":
+                round(PEAK_BF16_TFLOPS * ghz / max_ghz, 1) if max_ghz > 0 else None}
+
+
+def ingest_mfma(pmc_dir, workload_name):
+    """Adds the MFMA counter pass of one workload to the counter file."""
+    import synth
+    mf = mfma_from_dir(pmc_dir, synth.workload(workload_name).flop)
     entry = _update_entry(workload_name, {"mfma": mf})
     print(json.dumps(entry["mfma"]))
 
@@ -429,8 +434,8 @@ def main():
         ingest_mfma(args.ingest_mfma, args.workload)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(sharding across GPUs is described in the design notes, not built).",
+        print(f"bench.py: the library runs on one GPU; --gpus {args.gpus} is not supported "
+              "(sharding across GPUs is described in the design notes, not implemented).",
               file=sys.stderr)
         sys.exit(2)
     import torch
