@@ -34,6 +34,10 @@
  *     library: one buffer per device, grown on demand and kept until process exit.
  *     Growing it synchronises the device; callers that capture HIP graphs reserve it
  *     first with attn_reserve_workspace() or one uncaptured call of the same shape.
+ *     Every call that uses it (split-KV calls and attn_block_causal) shares that one
+ *     buffer: such calls must not run at the same time on different streams of one
+ *     device (order them on one stream, or synchronise between them); calls on one
+ *     stream are ordered by the stream.
  */
 #ifndef ATTN_DENSE_H
 #define ATTN_DENSE_H
