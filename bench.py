@@ -43,15 +43,16 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X published dense BF16 MFMA peak (2.5 PFLOP/s
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
 DEFAULT_WORKLOAD = "dense_b1_n4096_h32_d128"
 CSRC = "transformer_attention_dense_amd/csrc/"
-SHARED_SOURCES = ["attn_device.h", "attn_api.hip", "attn_launch.h"]
+# the build script too: its compiler flags change the kernels' code
+SHARED_SOURCES = ["attn_device.h", "attn_api.hip", "attn_launch.h", "../build.py"]
 KIND_SOURCES = {"na3d": ["attn_na3d.hip"]}
 DENSE_SOURCES = ["attn_kernels.hip", "attn_pingpong.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def kernel_source_hash(kind) -> str:
-    """Hash of the sources the kernels of one workload kind are built from: counter
-    readings taken on other sources are stale."""
+    """Hash of the sources (and build script) the kernels of one workload kind are built
+    from: counter readings taken on other sources are stale."""
     h = hashlib.sha256()
     for rel in SHARED_SOURCES + KIND_SOURCES.get(kind, DENSE_SOURCES):
         with open(os.path.join(ROOT, CSRC, rel), "rb") as f:

@@ -1,4 +1,8 @@
-"""Builds the HIP library (libattn_dense.so) for gfx950 in-tree with hipcc."""
+"""Builds the HIP library (libattn_dense.so) for gfx950 in-tree with hipcc.
+
+Each source is compiled to an object of its own (in parallel), with the flags common to
+all plus any per-source flags, and the objects are linked into the shared library.
+"""
 import os
 import shutil
 import subprocess
@@ -9,17 +13,28 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn_dense.so")
+OBJDIR = os.path.join(PKG, "_build")
 SOURCES = [os.path.join(CSRC, "attn_kernels.hip"), os.path.join(CSRC, "attn_pingpong.hip"),
            os.path.join(CSRC, "attn_na3d.hip"), os.path.join(CSRC, "attn_api.hip")]
 
 # Packed FP32 VALU forms are disabled for all device code: the compiler otherwise
 # emits them from ordinary float code.
-HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              # no NaN semantics are relied on (infinities are): lets max/min skip the
              # canonicalisation of their inputs
              "-fno-honor-nans",
              "-Wall", "-Wno-unused-command-line-argument"]
+
+# Per-source flags. The 2- and 4-wave kernels are scheduled for instruction-level
+# parallelism: B=1024 N=64 H=32 D=64 measured 6% faster (228 against 242 us), the other
+# workloads of these kernels within 1%; the ping-pong and neighborhood kernels measured
+# the same or slower with it and keep the default scheduler.
+PER_SOURCE_FLAGS = {
+    "attn_kernels.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+}
+
+LINK_FLAGS = ["--offload-arch=gfx950", "-shared", "-fPIC"]
 
 
 def hipcc() -> str:
@@ -30,13 +45,33 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    cmd = [hipcc()] + HIP_FLAGS + ["-I" + INCLUDE, "-I" + CSRC, "-o", LIB + ".tmp"] + SOURCES
+    cc = hipcc()
+    os.makedirs(OBJDIR, exist_ok=True)
+    jobs = []
+    for src in SOURCES:
+        name = os.path.basename(src)
+        obj = os.path.join(OBJDIR, name + ".o")
+        cmd = ([cc] + HIP_FLAGS + PER_SOURCE_FLAGS.get(name, []) +
+               ["-I" + INCLUDE, "-I" + CSRC, "-c", src, "-o", obj])
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        jobs.append((name, obj, subprocess.Popen(cmd, stdout=subprocess.PIPE,
+                                                 stderr=subprocess.STDOUT, text=True)))
+    failed = []
+    for name, _, proc in jobs:
+        out, _ = proc.communicate()
+        if proc.returncode != 0:
+            sys.stderr.write(out)
+            failed.append(name)
+    if failed:
+        raise RuntimeError("hipcc failed compiling " + ", ".join(failed))
+    cmd = [cc] + LINK_FLAGS + ["-o", LIB + ".tmp"] + [obj for _, obj, _ in jobs]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building libattn_dense.so")
+        raise RuntimeError("hipcc failed linking libattn_dense.so")
     os.replace(LIB + ".tmp", LIB)
     return LIB
 
