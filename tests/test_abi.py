@@ -106,14 +106,17 @@ def test_plan_for_the_workloads():
     assert p1["workspace_bytes"] == 0
     p3 = attn.attn_plan(1, 4096, 5120, 32, 128)
     assert p3["splits"] == 1 and p3["waves"] == 8 and p3["workgroups"] == 512
-    # D = 64 keeps two 4-wave workgroups per CU
+    # D = 64 as well when the 256-row blocks fill the GPU
     p2 = attn.attn_plan(2, 16384, 16384, 32, 64)
-    assert p2["waves"] == 4 and p2["workgroups"] == 128 * 64
+    assert p2["waves"] == 8 and p2["workgroups"] == 64 * 64 and p2["splits"] == 1
     # too few 256-row blocks, and fewer than 256 128-row blocks: 2-wave workgroups
     # (64 rows each); short sequences: 2 waves
     p0 = attn.attn_plan(1, 256, 256, 32, 64)
     assert p0["waves"] == 2 and p0["workgroups"] == 4 * 32 and p0["splits"] == 1
+    # 256 blocks of 256 rows: ping-pong; 256 blocks of 128 rows: 4 waves; fewer: 2 waves
+    assert attn.attn_plan(1, 1024, 1024, 64, 64)["waves"] == 8
     assert attn.attn_plan(1, 512, 512, 64, 64)["waves"] == 4
+    assert attn.attn_plan(1, 512, 512, 32, 64)["waves"] == 2
     assert attn.attn_plan(1024, 64, 64, 32, 64)["waves"] == 2
     # few query blocks and long keys -> the keys are split and a work space is needed
     ps = attn.attn_plan(1, 64, 8192, 2, 128)

@@ -61,15 +61,15 @@ int make_plan(int B, int Nq, int Nk, int H, int D, int num_splits, int waves, Pl
     const int key_tiles = (Nk + tile - 1) / tile;
     int w = waves;
     if (w == 0) {
-        // D = 128: the 8-wave ping-pong kernel (256 query rows per workgroup, one
-        // workgroup per CU) when it alone fills the 256 CUs. Otherwise, and for D = 64
-        // (where two 4-wave workgroups per CU measured faster), 4 waves; 2 waves for
-        // short query ranges and for grids of fewer than 256 4-wave workgroups (twice
-        // as many workgroups: B=1 N=256 H=32 D=64 measured 6.8 us against 7.4), with
-        // the keys split below when needed.
+        // The 8-wave ping-pong kernel (256 query rows per workgroup, one workgroup per
+        // CU) when it alone fills the 256 CUs: at D = 128, and at D = 64 too (2-5% faster
+        // than two 4-wave workgroups per CU on B=1..2, N=2048..16384, H=16..32; equal on
+        // B=4 N=1024). Otherwise 4 waves; 2 waves for short query ranges and for grids of
+        // fewer than 256 4-wave workgroups (twice as many workgroups: B=1 N=256 H=32
+        // D=64 measured 6.8 us against 7.4), with the keys split below when needed.
         const long long pp_blocks = (long long)((Nq + 255) / 256) * B * H;
         const long long blocks4 = (long long)((Nq + 127) / 128) * B * H;
-        if (D == 128 && Nq >= 256 && pp_blocks >= 256)
+        if (Nq >= 256 && pp_blocks >= 256)
             w = 8;
         else
             w = (Nq <= 64 || blocks4 < 256) ? 2 : 4;
