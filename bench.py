@@ -6,16 +6,20 @@ B=1 N=4096 H=32 D=128 (BF16 in and out, FP32 accumulation), i.e. one attn_dense
 call. FLOP per step = 4*B*H*Nq*Nk*D (the QK^T and PV contractions).
 
 Output: one JSON line (rank 0) with the metric, the roofline of the dominant kernel
-(timed with HIP events on the stream the kernel is launched on) and the FP64 CPU
-oracle timed on a bounded sample of the same workload.
+(timed with HIP events on the stream the kernel is launched on), the FP64 CPU oracle
+timed on a bounded sample of the same workload, the timed output checked against the
+oracle rows that sample computed, the inputs checked byte for byte after timing, the
+shader clock held under the load (measured in this run), and the environment.
 
-Defaults: 2000 warmup steps (about half a second of work at the default workload: the
-GPU's clock needs that long under load to settle) and 500 timed steps.
+Warmup: at least --warmup steps, continued until --warmup-seconds (default 0.5 s) of
+work have run: the GPU's clock takes that long under load to settle, and timed steps
+on a ramping clock measure the power controller, not the kernel. The line reports
+the steps and seconds actually run. Defaults: 2000 warmup steps, 500 timed steps.
 
 Options beyond the common ones:
   --workload NAME   another workload from synth.WORKLOADS (parity sizes)
-  --all             one JSON line per workload (no CPU baseline)
-  --no-cpu          skip the CPU oracle timing
+  --all             one JSON line per workload (CPU baseline on a shorter sample each)
+  --no-cpu          skip the CPU oracle timing (and the output check that uses it)
   --calib-mib MiB   before the timed steps, run a plain streaming kernel (torch.neg on
                     float32: reads and writes MiB each) `steps` times; rocprofv3 counter
                     runs use it to calibrate FETCH_SIZE / WRITE_SIZE
@@ -65,10 +69,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=2000)
+    ap.add_argument("--warmup-seconds", type=float, default=0.5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--all", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds-all", type=float, default=4.0)
     ap.add_argument("--calib-mib", type=int, default=0)
     ap.add_argument("--ingest", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--ingest-mfma", metavar="PMC_DIR")
@@ -116,24 +122,26 @@ def traffic_for(w):
     return counters_for(w).get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, seconds):
-    """FP64 oracle on a bounded sample of query rows of the same workload (all keys)."""
+def cpu_baseline(w, seconds, ts):
+    """FP64 oracle on a bounded sample of query rows of the same workload (all keys),
+    from the first row in [B, Nq, H] order. Returns the baseline record and the oracle's
+    output rows [done, D] (used to check the GPU's output)."""
     import numpy as np
     import oracle
-    ts = w.tensors()
     total_rows = w.B * w.Nq * w.H
     flop_per_row = 4 * w.keys * w.D
     chunk = 256
     done = 0
+    outs = []
     t0 = time.perf_counter()
     while True:
         rows = np.arange(done, min(done + chunk, total_rows), dtype=np.int64)
         if w.kind == "block_causal":
-            oracle.block_causal_rows(ts[0], ts[1], ts[2], ts[3], rows=rows)
+            outs.append(oracle.block_causal_rows(ts[0], ts[1], ts[2], ts[3], rows=rows))
         elif w.kind == "na3d":
-            oracle.na3d_rows(ts[0], ts[1], ts[2], w.kernel, rows=rows)
+            outs.append(oracle.na3d_rows(ts[0], ts[1], ts[2], w.kernel, rows=rows))
         else:
-            oracle.attention_rows(ts[0], ts[1], ts[2], *ts[3:5], rows=rows)
+            outs.append(oracle.attention_rows(ts[0], ts[1], ts[2], *ts[3:5], rows=rows))
         done += rows.size
         el = time.perf_counter() - t0
         if el >= seconds or done >= total_rows:
@@ -145,10 +153,87 @@ def cpu_baseline(w, seconds):
         rate = 4 * w.D * int(vis[(rows_done // w.H) % w.Nq].sum()) / el / 1e12
     else:
         rate = done * flop_per_row / el / 1e12
-    return {"value": rate, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{done} of {total_rows} query rows (first rows in [B,Nq,H] order) of "
-                      f"{w.name}, every {'visible ' if w.kind == 'block_causal' else ''}key, "
-                      f"FP64, {el:.1f} s"}
+    rec = {"value": rate, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+           "sample": f"{done} of {total_rows} query rows (first rows in [B,Nq,H] order) of "
+                     f"{w.name}, every {'visible ' if w.kind == 'block_causal' else ''}key, "
+                     f"FP64, {el:.1f} s"}
+    return rec, np.concatenate(outs)
+
+
+def check_output(out_bits, ref_rows, D):
+    """The pages' acceptance step on the timed output (page "Audit SGLang interfaces
+    and refresh validated kernel solutions", scripts/task_acceptance.py compare_output):
+    the first ref_rows.shape[0] rows of the GPU output against the FP64 oracle, under
+    the gate |err| <= 2e-2 + 2e-2 |ref| on >= 99.99% of elements, none above 1e-1, all
+    finite (the pages' own BF16 rule reported beside it)."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from acceptance import compare
+    n = ref_rows.shape[0]
+    res = compare(out_bits.reshape(-1, D)[:n], ref_rows)
+    res["rows_checked"] = n
+    res["rows_total"] = out_bits.size // D
+    return res
+
+
+def probe_library():
+    """The shader-clock probe (libattn_probe.so, include/attn_probe.h), or None."""
+    import ctypes
+    path = os.path.join(ROOT, "transformer_attention_dense_amd", "libattn_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.attn_probe_clock.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_void_p]
+    lib.attn_probe_clock.restype = ctypes.c_int
+    lib.attn_probe_realtime_mhz.argtypes = []
+    lib.attn_probe_realtime_mhz.restype = ctypes.c_double
+    return lib
+
+
+def enqueue_clock_probe(torch, stream, workgroups=256, ticks=2000):
+    """Enqueues the clock probe on `stream` (behind the launches already there); returns
+    a function giving the median shader clock in GHz once the stream has run it."""
+    lib = probe_library()
+    if lib is None:
+        return lambda: None
+    buf = torch.zeros(workgroups, dtype=torch.float32, device="cuda")
+    if lib.attn_probe_clock(buf.data_ptr(), workgroups, ticks, stream.cuda_stream) != 0:
+        return lambda: None
+    mhz = lib.attn_probe_realtime_mhz()
+
+    def read():
+        v = buf.cpu()
+        v = v[v > 0]
+        if v.numel() == 0 or mhz <= 0:
+            return None
+        return round(float(v.median()) * mhz / 1000.0, 3)
+    return read
+
+
+def environment(torch):
+    """The pages' report opens with an environment row (same page,
+    scripts/audit_solutions.py); this is that row for this run."""
+    import platform
+    env = {"gpu": torch.cuda.get_device_name(0), "torch": torch.__version__,
+           "hip": getattr(torch.version, "hip", None), "python": platform.python_version()}
+    try:
+        env["gpu_arch"] = torch.cuda.get_device_properties(0).gcnArchName
+        env["gpu_cus"] = torch.cuda.get_device_properties(0).multi_processor_count
+    except Exception:  # noqa: BLE001 - optional fields
+        pass
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            env["rocm"] = f.read().strip()
+    except OSError:
+        pass
+    try:
+        with open("/proc/cpuinfo") as f:
+            env["cpu"] = next(line.split(":", 1)[1].strip() for line in f
+                              if line.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
+    env["host_cores_available"] = len(os.sched_getaffinity(0))
+    return env
 
 
 def graph_timing(torch, call, out):
@@ -177,17 +262,32 @@ def graph_timing(torch, call, out):
         return {"graph_call_us": None, "graph_error": str(e)[:200]}
 
 
-def bench_one(w, steps, warmup, torch, attn):
-    ts = w.tensors()
+def device_bits(t, torch):
+    """BF16 (or int32) device tensor -> host numpy array of its raw bits."""
+    import numpy as np
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def bench_one(w, steps, warmup, warmup_seconds, torch, attn, ts):
+    import numpy as np
     if w.kind == "block_causal":  # Q, K, V bits and the int32 image ids
         dts = [to_device(t, torch) for t in ts[:3]] + [torch.from_numpy(ts[3]).cuda()]
     else:
         dts = [to_device(t, torch) for t in ts]
     out, call = make_call(w, dts, attn)
     stream = torch.cuda.current_stream()
-    for _ in range(warmup):
-        call()
+    # warmup: at least `warmup` steps and at least `warmup_seconds` of them
     torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    done = 0
+    while done < warmup or time.perf_counter() - w0 < warmup_seconds:
+        for _ in range(max(1, min(warmup - done, 200)) if done < warmup else 50):
+            call()
+            done += 1
+        torch.cuda.synchronize()
+    warm = {"warmup_steps_run": done, "warmup_s": round(time.perf_counter() - w0, 3)}
     # whole-job timing: exactly `steps` steps between synchronisations
     t0 = time.perf_counter()
     ev0 = torch.cuda.Event(enable_timing=True)
@@ -196,9 +296,14 @@ def bench_one(w, steps, warmup, torch, attn):
     for _ in range(steps):
         call()
     ev1.record(stream)
+    clock = enqueue_clock_probe(torch, stream)  # right behind the timed launches
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ev_ms = ev0.elapsed_time(ev1)
+    clock_ghz = clock()
+    timed_out = device_bits(out, torch)  # the output the timed steps wrote
+    inputs_unchanged = all(np.array_equal(device_bits(d, torch), np.ascontiguousarray(t))
+                           for d, t in zip(dts, ts))
     # per-call event timing (the pages' eager method: median of event-bracketed calls)
     samples = []
     for _ in range(min(steps, 50)):
@@ -223,7 +328,9 @@ def bench_one(w, steps, warmup, torch, attn):
     finite = bool(torch.isfinite(out.float()).all())
     graph = graph_timing(torch, call, out)
     return {"wall_s": wall, "event_ms": ev_ms, "median_call_us": statistics.median(samples),
-            "plan": plan, "finite": finite, "graph": graph}
+            "plan": plan, "finite": finite, "graph": graph, "warm": warm,
+            "clock_ghz": clock_ghz, "timed_out": timed_out,
+            "inputs_unchanged": inputs_unchanged}
 
 
 def kernel_name(D, plan):
@@ -241,12 +348,13 @@ def kernel_name(D, plan):
     return main if plan["splits"] == 1 else main + f" + attn_combine_kernel<{D}>"
 
 
-def record(w, r, steps, warmup, cpu):
+def record(w, r, steps, warmup, cpu, check, env):
     ms_per_step = r["wall_s"] * 1000.0 / steps
     value = w.flop * steps / r["wall_s"] / 1e12
     launch_us = r["event_ms"] * 1000.0 / steps  # average duration per launch on the stream
     achieved = w.flop / (launch_us * 1e-6) / 1e12
-    hbm = traffic_for(w)
+    stored = counters_for(w)
+    hbm = stored.get("hbm_bytes_per_launch")
     rec = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -265,6 +373,7 @@ def record(w, r, steps, warmup, cpu):
                    "splits": r["plan"]["splits"], "waves": r["plan"]["waves"],
                    "workgroups": r["plan"]["workgroups"]},
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        **r["warm"],
         "median_call_us": round(r["median_call_us"], 2),
         **r["graph"],
         "roofline": {
@@ -274,26 +383,38 @@ def record(w, r, steps, warmup, cpu):
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": hbm,
+            "traffic_source": (f"profiles/traffic.json (counter runs on kernel sources "
+                               f"{stored.get('kernel_source_hash')})" if hbm else None),
             "kernel": kernel_name(w.D, r["plan"]),
             "avg_launch_us": round(launch_us, 2),
             "algorithmic_flop_per_launch": w.flop,
             "algorithmic_bytes_per_launch": w.algorithmic_bytes,
             "hbm_gbs_algorithmic": round(w.algorithmic_bytes / (launch_us * 1e-6) / 1e9, 1),
         },
+        "clock_ghz_after_timed_steps": r["clock_ghz"],
         "outputs_finite": r["finite"],
+        "inputs_unchanged": r["inputs_unchanged"],
     }
     if w.flop / w.algorithmic_bytes < 315:  # below the ridge point: HBM bound
         rec["roofline"].update({"bound": "hbm", "achieved": rec["roofline"]["hbm_gbs_algorithmic"],
                                 "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                 "frac": round(rec["roofline"]["hbm_gbs_algorithmic"]
                                               / PEAK_HBM_GBS, 4)})
-    mf = counters_for(w).get("mfma")
+    mf = stored.get("mfma")
     if mf and rec["roofline"]["bound"] == "mfma" and mf["profiled_duration_us"] >= 100:
-        # From a separate counter run of the same kernel source (counters perturb timing).
-        # GRBM_GUI_ACTIVE also counts some 13-16 thousand cycles per dispatch outside the
-        # kernel's own time stamps, so these read a few percent off for long kernels and
-        # mean nothing for short ones, which are left out.
-        rec["roofline"].update({"mfma_util": mf["mfma_util"], "clock_ghz": mf["clock_ghz"]})
+        # Not measured in this run: from a separate, committed counter run of the same
+        # kernel sources (counters perturb timing). GRBM_GUI_ACTIVE also counts some
+        # 13-16 thousand cycles per dispatch outside the kernel's own time stamps, so
+        # these read a few percent off for long kernels and mean nothing for short ones,
+        # which are left out.
+        rec["stored_counters"] = {
+            "source": "profiles/traffic.json", "kernel_source_hash": stored["kernel_source_hash"],
+            "mfma_util": mf["mfma_util"], "clock_ghz": mf["clock_ghz"],
+            "profiled_duration_us": mf["profiled_duration_us"]}
+    if check is not None:
+        rec["output_check"] = check
+    if env is not None:
+        rec["environment"] = env
     if w.kind == "na3d":
         rec["config"].update({"grid": list(w.grid), "kernel": list(w.kernel)})
     if cpu is not None:
@@ -456,17 +577,21 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    env = environment(torch)
     names = [w.name for w in synth.WORKLOADS] if args.all else [args.workload]
     for name in names:
         w = synth.workload(name)
-        print(f"bench: {w.name} warmup {args.warmup} steps {args.steps}", file=sys.stderr,
-              flush=True)
-        r = bench_one(w, args.steps, args.warmup, torch, attn)
-        cpu = None
-        if not args.all and not args.no_cpu:
+        print(f"bench: {w.name} warmup {args.warmup} steps / {args.warmup_seconds} s, "
+              f"timed steps {args.steps}", file=sys.stderr, flush=True)
+        ts = w.tensors()
+        r = bench_one(w, args.steps, args.warmup, args.warmup_seconds, torch, attn, ts)
+        cpu = check = None
+        if not args.no_cpu:
             print("bench: timing the FP64 CPU oracle on a sample", file=sys.stderr, flush=True)
-            cpu = cpu_baseline(w, args.cpu_seconds)
-        print(json.dumps(record(w, r, args.steps, args.warmup, cpu)), flush=True)
+            cpu, ref_rows = cpu_baseline(
+                w, args.cpu_seconds_all if args.all else args.cpu_seconds, ts)
+            check = check_output(r["timed_out"], ref_rows, w.D)
+        print(json.dumps(record(w, r, args.steps, args.warmup, cpu, check, env)), flush=True)
 
 
 if __name__ == "__main__":

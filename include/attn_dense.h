@@ -28,16 +28,24 @@
  *     synchronisation. Results are deterministic: the same inputs and the same launch
  *     plan give the same bits.
  *   - Return value: ATTN_OK (0) or a negative ATTN_ERR_* code. All argument checks run
- *     before any HIP call, so an invalid call touches no device state. No exception
- *     crosses the ABI.
- *   - Split-KV work space (used when the grid would underfill the GPU) is owned by the
- *     library: one buffer per device, grown on demand and kept until process exit.
- *     Growing it synchronises the device; callers that capture HIP graphs reserve it
- *     first with attn_reserve_workspace() or one uncaptured call of the same shape.
- *     Every call that uses it (split-KV calls and attn_block_causal) shares that one
- *     buffer: such calls must not run at the same time on different streams of one
- *     device (order them on one stream, or synchronise between them); calls on one
- *     stream are ordered by the stream.
+ *     before any work is enqueued (the only HIP call before them asks for the current
+ *     device), so an invalid call touches no device state. No exception crosses the ABI.
+ *   - Work space (split-KV partial results when the grid would underfill the GPU, and
+ *     the image-id summaries of attn_block_causal), per device, from one of two sources:
+ *       * the caller's buffer, if attn_set_workspace() gave one for the current device:
+ *         used as is, never grown or freed; a call that needs more returns
+ *         ATTN_ERR_WORKSPACE, a buffer overlapping the call's tensors ATTN_ERR_ALIAS;
+ *       * otherwise the library's own buffer, allocated with hipMalloc when a call
+ *         needs more than it holds (at least doubling). A superseded buffer is never
+ *         freed (launches in flight and HIP graphs captured earlier keep using it), so
+ *         growing never synchronises the device. Allocation is not allowed during HIP
+ *         graph capture: callers that capture reserve the space first, with
+ *         attn_reserve_workspace() or one uncaptured call of the same shape, or supply
+ *         their own buffer.
+ *     Every call that uses the work space on a device shares that one buffer: such
+ *     calls must not run at the same time on different streams of one device (order
+ *     them on one stream, or give each stream its own buffer through
+ *     attn_set_workspace() before its calls); calls on one stream are ordered by it.
  */
 #ifndef ATTN_DENSE_H
 #define ATTN_DENSE_H
@@ -53,9 +61,9 @@ extern "C" {
 #define ATTN_ERR_SHAPE (-2)       /* B, N, H < 1, or Np < 0 */
 #define ATTN_ERR_UNSUPPORTED (-3) /* D not in {64, 128}, or a bad launch option */
 #define ATTN_ERR_ALIGN (-4)       /* a pointer is not 16-byte aligned */
-#define ATTN_ERR_ALIAS (-5)       /* the output overlaps an input */
+#define ATTN_ERR_ALIAS (-5)       /* the output (or a caller's work space) overlaps an input */
 #define ATTN_ERR_OVERFLOW (-6)    /* a size exceeds the index range of the kernels */
-#define ATTN_ERR_WORKSPACE (-7)   /* the split-KV work space could not be allocated */
+#define ATTN_ERR_WORKSPACE (-7)   /* the work space could not be allocated or is too small */
 #define ATTN_ERR_HIP (-8)         /* a HIP runtime call or kernel launch failed */
 
 /*
@@ -92,8 +100,7 @@ int attn_cross(const void* q, const void* k, const void* v, void* out, int B, in
  * blocks, but any ids are handled exactly). Scale D^-0.5.
  * q, k, v: [B, N, H, D] BF16; image_ids: [N] int32 in device memory, shared by the
  * batch, 16-byte aligned; out: [B, N, H, D] BF16, must overlap no input.
- * Uses the library's per-device work space (16 bytes per 32 rows) for summaries of
- * the ids; growing it synchronises the device, as for split-KV calls.
+ * Uses the device's work space (16 bytes per 32 rows) for summaries of the ids.
  */
 int attn_block_causal(const void* q, const void* k, const void* v, const int* image_ids,
                       void* out, int B, int N, int H, int D, void* stream);
@@ -155,11 +162,29 @@ int attn_na3d_plan(int B, int T, int Y, int X, int H, int D, int kt, int ky, int
                    int* query_cols, long long* workgroups);
 
 /*
- * Makes sure the current device's split-KV work space holds at least `bytes`
- * (allocating and synchronising the device if it must grow). Returns ATTN_OK,
- * ATTN_ERR_WORKSPACE or ATTN_ERR_HIP.
+ * Makes sure the current device's work space holds at least `bytes`: grows the
+ * library's buffer if it is smaller (no device synchronisation), or, when the caller
+ * supplied the buffer, checks that it is large enough. Returns ATTN_OK,
+ * ATTN_ERR_WORKSPACE (allocation failed, or the caller's buffer is too small) or
+ * ATTN_ERR_HIP (no current device).
  */
 int attn_reserve_workspace(long long bytes);
+
+/*
+ * Caller-supplied work space for the current device (the pages keep engine set-up
+ * such as work spaces out of the timed call: page "SGLang interface and
+ * implementation audit - 2026-10-19", section "Validation and timing").
+ *   ptr:   device memory of the current device, 256-byte aligned, `bytes` long; the
+ *          caller owns it and must keep it allocated while calls that use it may still
+ *          run (including replays of HIP graphs captured with it). NULL reverts to the
+ *          library's own buffer.
+ *   bytes: its size; attn_plan() reports what a call needs (workspace_bytes), and a
+ *          block-causal call needs 16 bytes per 32 rows.
+ * Later calls on this device, from any thread, use it until the next
+ * attn_set_workspace(). Returns ATTN_OK, ATTN_ERR_ALIGN (ptr not 256-byte aligned),
+ * ATTN_ERR_SHAPE (bytes < 0) or ATTN_ERR_HIP (no current device).
+ */
+int attn_set_workspace(void* ptr, long long bytes);
 
 /* Static description of an error code (never NULL). */
 const char* attn_strerror(int code);

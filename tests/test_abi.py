@@ -29,6 +29,25 @@ def test_header_declares_the_abi_and_library_exports_it():
         assert hasattr(lib, n), f"missing export {n}"
 
 
+def test_probe_library_exports_its_header_and_checks_arguments():
+    """The benchmark's clock probe: a library of its own (not the attention ABI) that
+    exports what include/attn_probe.h declares and rejects bad arguments before any
+    HIP call."""
+    import ctypes
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "attn_probe.h")).read(),
+                  flags=re.S)
+    names = re.findall(r"^\s*\w+\s*\*?\s*(attn_\w+)\s*\(", text, flags=re.M)
+    assert set(names) == {"attn_probe_clock", "attn_probe_realtime_mhz"}
+    lib = ctypes.CDLL(os.path.join(ROOT, "transformer_attention_dense_amd", "libattn_probe.so"))
+    for n in names:
+        assert hasattr(lib, n)
+    lib.attn_probe_clock.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_void_p]
+    assert lib.attn_probe_clock(None, 256, 2000, None) == -1
+    assert lib.attn_probe_clock(A, 0, 2000, None) == -2
+    assert lib.attn_probe_clock(A, 256, 0, None) == -2
+
+
 def test_error_codes_match_header():
     text = open(HEADER).read()
     codes = dict((int(v), k) for k, v in re.findall(r"#define (ATTN_ERR_\w+) \((-\d+)\)", text))
@@ -117,6 +136,25 @@ def test_plan_for_the_workloads():
     assert attn.attn_plan(1, 1024, 1024, 64, 64)["waves"] == 8
     assert attn.attn_plan(1, 512, 512, 64, 64)["waves"] == 4
     assert attn.attn_plan(1, 512, 512, 32, 64)["waves"] == 2
+    # exactly 256 blocks of 256 rows: one 8-wave workgroup per CU, no key split
+    for B, N, H, D in [(1, 2048, 32, 64), (1, 2048, 32, 128), (2, 1024, 32, 128),
+                       (1, 4096, 16, 128)]:
+        assert attn.attn_plan(B, N, N, H, D) == {"splits": 1, "waves": 8, "workgroups": 256,
+                                                 "workspace_bytes": 0}, (B, N, H, D)
+    # an explicit 8-wave launch on a small grid splits the keys up to 256 workgroups
+    p8 = attn.attn_plan(1, 512, 8192, 32, 128, waves=8)
+    assert p8["waves"] == 8 and p8["workgroups"] == 256 and p8["splits"] == 4
+
+
+def test_set_workspace_checks_before_any_device_work():
+    assert attn.attn_set_workspace(A + 16, 1 << 20) == -4   # not 256-byte aligned
+    assert attn.attn_set_workspace(A, -1) == -2
+    # without a GPU the current device cannot be found; with one this sets a buffer
+    # that the test immediately withdraws again
+    rc = attn.attn_set_workspace(A, 1 << 20)
+    assert rc in (0, -8)
+    if rc == 0:
+        assert attn.attn_set_workspace(None, 0) == 0
     assert attn.attn_plan(1024, 64, 64, 32, 64)["waves"] == 2
     # few query blocks and long keys -> the keys are split and a work space is needed
     ps = attn.attn_plan(1, 64, 8192, 2, 128)

@@ -74,3 +74,31 @@ def test_counter_readings_are_dropped_when_sources_change(tmp_path, monkeypatch)
     e = bench.counters_for(w)
     assert e["hbm_bytes_per_launch"] == 7 and "mfma" not in e
     assert e["kernel_source_hash"] == bench.kernel_source_hash(w.kind)
+
+
+def test_output_check_applies_the_acceptance_rule():
+    """The bench's check of its timed output: the oracle's own rows rounded to BF16 pass,
+    the same rows with one element off by 0.5 fail (the per-element cap)."""
+    import numpy as np
+
+    import synth
+    w = synth.small("dense", 1, 64, 2, 64, 950, sigma_qk=2.0)
+    ts = w.tensors()
+    cpu, ref = bench.cpu_baseline(w, 0.0, ts)
+    assert ref.shape == (w.B * w.Nq * w.H, w.D) and cpu["kind"] == "oracle"
+    bits = synth.f32_to_bf16_bits(ref.astype(np.float32))
+    good = bench.check_output(bits, ref, w.D)
+    assert good["ok"] and good["rows_checked"] == good["rows_total"] == 128
+    bad = synth.bf16_bits_to_f32(bits).copy()
+    bad[7, 3] += 0.5
+    res = bench.check_output(synth.f32_to_bf16_bits(bad), ref, w.D)
+    assert not res["ok"] and res["max_abs_err"] > 0.4
+
+
+def test_output_check_covers_only_the_rows_the_oracle_computed():
+    import numpy as np
+    ref = np.zeros((3, 64))
+    out = np.zeros((10, 64), np.uint16)
+    out[5:] = 0x4000  # 2.0 in BF16, beyond the checked rows
+    res = bench.check_output(out, ref, 64)
+    assert res["ok"] and res["rows_checked"] == 3 and res["rows_total"] == 10

@@ -1,7 +1,10 @@
 """GPU parity: the HIP library through its C ABI against the FP64 oracle.
 
-Small shapes compare every element; the six workloads at full size compare sampled
-rows (the oracle computes rows one by one) plus properties that hold at any size.
+Small shapes compare every element. The workloads at full size compare every element
+too, except the one whose oracle would take minutes (B=2 N=16384 H=32 D=64, 4.4e12
+multiply-adds): there every wave of 32 query rows of every head contributes one
+randomly chosen row (plus edge rows), so a mis-mapped workgroup or wave cannot go
+unseen. Properties that hold at any size are checked on the whole output as well.
 Every input is seeded (synth), identical bits feed both sides.
 """
 import sys
@@ -220,15 +223,25 @@ def test_invalid_call_leaves_output_untouched():
 
 # ---------------------------------------------------------------- the workloads, full size
 
-def sample_rows(w, count, seed):
-    total = w.B * w.Nq * w.H
+# Oracle work (multiply-adds x 2) up to which a full-size workload is compared on every
+# element: the FP64 oracle runs ~3.5e10 of them per second on 16 host cores, so the
+# largest such workload (B=8 N=1999 H=32 D=128, 5.2e11) takes ~15 s.
+FULL_CHECK_FLOP = 1.2e12
+
+
+def rows_per_wave(w, seed):
+    """One random query row from every block of 32 consecutive rows of every (b, h) (a
+    wave's rows in every kernel), plus the first, middle and last rows of each batch for
+    every head."""
     rng = np.random.default_rng(seed)
-    rows = set(rng.choice(total, size=min(count, total), replace=False).tolist())
-    # first and last query of every batch, for several heads, and the tail query block
+    blocks = -(-w.Nq // 32)
+    rows = set()
     for b in range(w.B):
-        for i in (0, w.Nq - 1, max(0, w.Nq - 33), w.Nq // 2):
-            for h in (0, w.H - 1, w.H // 2):
-                rows.add((b * w.Nq + i) * w.H + h)
+        for h in range(w.H):
+            i = np.minimum(np.arange(blocks) * 32 + rng.integers(0, 32, size=blocks), w.Nq - 1)
+            rows.update(((b * w.Nq + i) * w.H + h).tolist())
+            for e in (0, w.Nq // 2, w.Nq - 1):
+                rows.add((b * w.Nq + e) * w.H + h)
     return np.array(sorted(rows), dtype=np.int64)
 
 
@@ -259,9 +272,9 @@ def test_workload_full_size(idx):
     o = out.float()
     assert bool((o >= vmin[:, None] - 1e-2).all()) and bool((o <= vmax[:, None] + 1e-2).all())
     got = host(out).reshape(-1, w.D)
-    say(f"workload {w.name}: oracle rows")
-    rows = None if w.B * w.Nq * w.H * w.keys * w.D <= (1 << 30) else \
-        sample_rows(w, 1500, 800 + idx)
+    rows = None if w.flop <= FULL_CHECK_FLOP else rows_per_wave(w, 800 + idx)
+    say(f"workload {w.name}: oracle, "
+        f"{'every row' if rows is None else f'{rows.size} rows (one per wave)'}")
     if w.kind == "block_causal":
         ref = oracle.block_causal_rows(ts[0], ts[1], ts[2], ts[3], rows=rows)
     else:
@@ -282,10 +295,10 @@ def check_na3d_full_size(w, ts, idx):
     o = out.float().flatten(1, 3)
     assert bool((o >= vmin[:, None] - 1e-2).all()) and bool((o <= vmax[:, None] + 1e-2).all())
     got = host(out).reshape(-1, w.D)
-    say(f"workload {w.name}: oracle rows")
-    rows = sample_rows(w, 3000, 800 + idx)
-    ref = oracle.na3d_rows(ts[0], ts[1], ts[2], w.kernel, rows=rows)
-    res = assert_accepted(got[rows], ref, w.name)
+    assert w.flop <= FULL_CHECK_FLOP
+    say(f"workload {w.name}: oracle, every row")
+    ref = oracle.na3d_rows(ts[0], ts[1], ts[2], w.kernel)
+    res = assert_accepted(got, ref, w.name)
     say(f"workload {w.name}: {res}")
 
 
@@ -382,3 +395,139 @@ def test_graph_capture_replays_match_eager():
             g.replay()
             scratch.mul_(1.0001)  # unrelated eager work between replays
             assert np.array_equal(host(static_out), ref), f"{name}: replay {r} differs"
+
+
+# ---------------------------------------------------------------- work space
+
+def test_work_space_allocation_failure_leaves_output_untouched(monkeypatch):
+    """With allocation failing (fault injection), a split-KV call that needs a larger
+    work space than any call before it returns ATTN_ERR_WORKSPACE and writes nothing."""
+    attn.set_workspace(None)
+    B, Nq, Nk, H, D, splits = 1, 1024, 16384, 4, 128, 256
+    need = attn.attn_plan(B, Nq, Nk, H, D, num_splits=splits)["workspace_bytes"]
+    assert need > 512 << 20  # more than any other call of this suite reserves
+    say(f"work-space failure case: B{B} Nq{Nq} Nk{Nk} H{H} D{D} splits{splits}, {need} bytes")
+    q = dev(synth.normal_bf16((B, Nq, H, D), 760))
+    kv = dev(synth.normal_bf16((B, Nk, H, D), 761))
+    out = torch.full_like(q, 5.0)
+    monkeypatch.setenv("ATTN_TEST_FAIL_ALLOC", "1")
+    with pytest.raises(attn.AttnError) as e:
+        attn.fwd_ex(q, kv, kv, out=out, num_splits=splits)
+    assert e.value.code == -7
+    assert attn.attn_reserve_workspace(need) == -7
+    torch.cuda.synchronize()
+    assert bool((out == 5.0).all())
+    monkeypatch.delenv("ATTN_TEST_FAIL_ALLOC")
+
+
+def test_caller_work_space_used_and_checked():
+    """attn_set_workspace: a split-KV call runs in the caller's buffer (same bits as in
+    the library's), a too small buffer gives ATTN_ERR_WORKSPACE, one overlapping the
+    call's tensors ATTN_ERR_ALIAS, and None reverts to the library's buffer."""
+    B, N, H, D = 1, 300, 2, 128
+    w = synth.small("dense", B, N, H, D, 770, sigma_qk=2.0)
+    tq, tk, tv = (dev(t) for t in w.tensors())
+    need = attn.attn_plan(B, N, N, H, D, num_splits=3)["workspace_bytes"]
+    ref = host(attn.fwd_ex(tq, tk, tv, num_splits=3)).copy()
+    buf = torch.empty(need, dtype=torch.uint8, device="cuda")
+    try:
+        attn.set_workspace(buf)
+        assert np.array_equal(host(attn.fwd_ex(tq, tk, tv, num_splits=3)), ref)
+        attn.set_workspace(buf[:need - 256])
+        with pytest.raises(attn.AttnError) as e:
+            attn.fwd_ex(tq, tk, tv, num_splits=3)
+        assert e.value.code == -7
+        big = torch.empty(need + tq.numel() * 2 + 4096, dtype=torch.uint8, device="cuda")
+        outv = big[-tq.numel() * 2:].view(torch.bfloat16).view(tq.shape)
+        attn.set_workspace(big)
+        with pytest.raises(attn.AttnError) as e:
+            attn.fwd_ex(tq, tk, tv, out=outv, num_splits=3)
+        assert e.value.code == -5
+        with pytest.raises(attn.AttnError) as e:
+            attn.set_workspace(buf[1:])
+        assert e.value.code == -4
+    finally:
+        attn.set_workspace(None)
+    assert np.array_equal(host(attn.fwd_ex(tq, tk, tv, num_splits=3)), ref)
+
+
+def test_graph_capture_with_caller_work_space():
+    """A split-KV call captured in a HIP graph with a caller-supplied work space (no
+    allocation inside the capture) replays to the eager bits, with eager work between
+    the replays; block-causal summaries in the caller's buffer likewise."""
+    B, N, H, D = 1, 520, 3, 64
+    w = synth.small("dense", B, N, H, D, 780, sigma_qk=2.0)
+    tq, tk, tv = (dev(t) for t in w.tensors())
+    ids = torch.from_numpy(ids_from([("text", 20), ("image", 400), ("text", 100)])).cuda()
+    need = attn.attn_plan(B, N, N, H, D, num_splits=5)["workspace_bytes"]
+    buf = torch.empty(need, dtype=torch.uint8, device="cuda")
+    calls = {"split_kv": lambda out: attn.fwd_ex(tq, tk, tv, out=out, num_splits=5),
+             "block_causal": lambda out: attn.block_causal(tq, tk, tv, ids, out=out)}
+    other = torch.ones(1 << 20, device="cuda")
+    try:
+        attn.set_workspace(buf)
+        for name, call in calls.items():
+            say(f"graph capture with caller work space: {name}")
+            eager = torch.empty_like(tq)
+            call(eager)
+            ref = host(eager).copy()
+            static_out = torch.zeros_like(tq)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                call(static_out)
+            for r in range(3):
+                static_out.zero_()
+                g.replay()
+                other.mul_(1.0001)
+                assert np.array_equal(host(static_out), ref), f"{name}: replay {r} differs"
+    finally:
+        attn.set_workspace(None)
+
+
+# ---------------------------------------------------------------- launch plans at the GPU's size
+
+@pytest.mark.parametrize("B,N,H,D", [(1, 2048, 32, 128), (2, 1024, 32, 64)])
+def test_grids_of_one_workgroup_per_cu_do_not_split(B, N, H, D):
+    """256 blocks of 256 query rows fill the GPU's 256 CUs with the 8-wave kernel (one
+    workgroup per CU): one key range, no combine step, and every element correct."""
+    plan = attn.attn_plan(B, N, N, H, D)
+    assert plan == {"splits": 1, "waves": 8, "workgroups": 256, "workspace_bytes": 0}
+    say(f"256-workgroup plan: B{B} N{N} H{H} D{D}")
+    w = synth.small("dense", B, N, H, D, 790 + D)
+    q, k, v = w.tensors()
+    got = host(attn.dense(dev(q), dev(k), dev(v)))
+    assert_accepted(got, oracle.attention(q, k, v), f"256 workgroups B{B} N{N} D{D}")
+
+
+# ---------------------------------------------------------------- nonfinite inputs
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("splits,waves", [(1, 0), (3, 4), (1, 8)])
+def test_nonfinite_inputs_propagate_like_the_definition(D, splits, waves):
+    """NaN and infinity are not special-cased: the nonfinite outputs are exactly the
+    elements the definition (the FP64 oracle) makes nonfinite, and every other element
+    passes the acceptance rule. A NaN in a key row poisons every row of its head; +inf
+    in one key dimension makes the rows whose query has a positive entry there NaN
+    (the score is +inf, and inf - inf appears in the softmax), while rows with a
+    negative entry give that key weight 0; a NaN in a query row poisons that row only;
+    an inf in a value row makes that dimension infinite for every row of its head."""
+    B, N, H = 1, 150, 4
+    w = synth.small("dense", B, N, H, D, 795 + D, sigma_qk=1.0)
+    q, k, v = (t.copy() for t in w.tensors())
+    nan, pinf = np.uint16(0x7FC0), np.uint16(0x7F80)
+    k[0, 37, 0, 5] = nan          # head 0: every row NaN
+    k[0, 91, 1, 3] = pinf         # head 1: rows with q[., 3] > 0 NaN, < 0 unaffected
+    q[0, 10, 2, :] = 0
+    q[0, 10, 2, 7] = nan          # head 2: row 10 only
+    v[0, 120, 3, 9] = pinf        # head 3: dimension 9 infinite in every row
+    say(f"nonfinite case D{D} splits{splits} waves{waves}")
+    ref = oracle.attention(q, k, v)
+    got = bf16_bits_to_f64(run_ex(q, k, v, splits=splits, waves=waves))
+    bad_ref, bad_got = ~np.isfinite(ref), ~np.isfinite(got)
+    assert bad_ref[0, :, 0].all() and not bad_ref[0, :, 2][np.arange(N) != 10].any()
+    assert bad_ref[0, :, 3, 9].all() and 0 < bad_ref[0, :, 1].all(axis=-1).sum() < N
+    assert np.array_equal(bad_got, bad_ref), (
+        f"{int((bad_got != bad_ref).sum())} elements differ in finiteness")
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    fin = ~bad_ref
+    assert_accepted(got[fin], ref[fin], f"nonfinite case D{D}, finite elements")

@@ -7,11 +7,12 @@ library is missing or fails to load, importing the low-level functions raises.
 Low-level functions (same names and arguments as the C ABI; tensors passed as raw
 device addresses, ``stream`` as an integer hipStream_t):
     attn_dense, attn_prefix, attn_cross, attn_block_causal, attn_na3d, attn_fwd_ex,
-    attn_plan, attn_na3d_plan, attn_reserve_workspace, attn_strerror, attn_abi_version
+    attn_plan, attn_na3d_plan, attn_reserve_workspace, attn_set_workspace, attn_strerror,
+    attn_abi_version
 
 Tensor-level helpers (torch is used for device memory and the current stream):
     dense(q, k, v, out=None), prefix(q, kp, vp, kc, vc, out=None),
-    cross(q, k, v, out=None), fwd_ex(...)
+    cross(q, k, v, out=None), fwd_ex(...), set_workspace(buffer_or_None)
 Operations follow page "Audit SGLang interfaces and refresh validated kernel
 solutions": definitions/dense_attention/noncausal_dense_attention_h32_d{64,128}.json
 and definitions/block_causal_attention/prefix_cached_block_causal_h32_d128.json.
@@ -37,7 +38,8 @@ ERRORS = {
 # Exported symbols, in header order.
 SYMBOLS = ("attn_dense", "attn_prefix", "attn_cross", "attn_block_causal", "attn_na3d",
            "attn_fwd_ex",
-           "attn_plan", "attn_na3d_plan", "attn_reserve_workspace", "attn_strerror", "attn_abi_version")
+           "attn_plan", "attn_na3d_plan", "attn_reserve_workspace", "attn_set_workspace",
+           "attn_strerror", "attn_abi_version")
 
 
 class AttnError(RuntimeError):
@@ -69,6 +71,7 @@ def library() -> ctypes.CDLL:
                               ctypes.POINTER(ll), ctypes.POINTER(ll)]
     lib.attn_na3d_plan.argtypes = [i] * 9 + [ctypes.POINTER(i), ctypes.POINTER(ll)]
     lib.attn_reserve_workspace.argtypes = [ll]
+    lib.attn_set_workspace.argtypes = [p, ll]
     lib.attn_strerror.argtypes = [i]
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_abi_version.argtypes = []
@@ -131,6 +134,10 @@ def attn_plan(B, Nq, Nk, H, D, num_splits=0, waves=0):
 
 def attn_reserve_workspace(nbytes) -> int:
     return library().attn_reserve_workspace(nbytes)
+
+
+def attn_set_workspace(ptr, nbytes) -> int:
+    return library().attn_set_workspace(ptr, nbytes)
 
 
 def attn_strerror(code) -> str:
@@ -312,3 +319,22 @@ def fwd_ex(q, k0, v0, k1=None, v1=None, out=None, num_splits=0, waves=0):
     if rc != ATTN_OK:
         raise AttnError(rc, "attn_fwd_ex")
     return out
+
+
+def set_workspace(buf):
+    """Hands the library a caller-owned work space for buf's device (a contiguous GPU
+    tensor of any dtype, e.g. torch.empty(nbytes, dtype=torch.uint8, device=...)), or
+    reverts the current device to the library's own buffer with None. The caller keeps
+    buf alive while calls that use it may still run."""
+    torch = _t()
+    if buf is None:
+        rc = attn_set_workspace(None, 0)
+    else:
+        if not isinstance(buf, torch.Tensor) or buf.device.type != "cuda" or \
+                not buf.is_contiguous():
+            raise ValueError("the work space must be a contiguous GPU tensor")
+        if buf.device.index != torch.cuda.current_device():
+            raise ValueError("the work space must be on the current device")
+        rc = attn_set_workspace(buf.data_ptr(), buf.numel() * buf.element_size())
+    if rc != ATTN_OK:
+        raise AttnError(rc, "attn_set_workspace")

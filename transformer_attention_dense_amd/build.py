@@ -1,7 +1,9 @@
-"""Builds the HIP library (libattn_dense.so) for gfx950 in-tree with hipcc.
+"""Builds the HIP libraries for gfx950 in-tree with hipcc: libattn_dense.so (the
+attention library, include/attn_dense.h) and libattn_probe.so (the benchmark's shader
+clock probe, include/attn_probe.h).
 
 Each source is compiled to an object of its own (in parallel), with the flags common to
-all plus any per-source flags, and the objects are linked into the shared library.
+all plus any per-source flags, and the objects are linked into the shared libraries.
 """
 import os
 import shutil
@@ -16,6 +18,8 @@ LIB = os.path.join(PKG, "libattn_dense.so")
 OBJDIR = os.path.join(PKG, "_build")
 SOURCES = [os.path.join(CSRC, "attn_kernels.hip"), os.path.join(CSRC, "attn_pingpong.hip"),
            os.path.join(CSRC, "attn_na3d.hip"), os.path.join(CSRC, "attn_api.hip")]
+PROBE_LIB = os.path.join(PKG, "libattn_probe.so")
+PROBE_SOURCES = [os.path.join(CSRC, "attn_probe.hip")]
 
 # Packed FP32 VALU forms are disabled for all device code: the compiler otherwise
 # emits them from ordinary float code.
@@ -48,31 +52,33 @@ def build(verbose: bool = False) -> str:
     cc = hipcc()
     os.makedirs(OBJDIR, exist_ok=True)
     jobs = []
-    for src in SOURCES:
+    for src in SOURCES + PROBE_SOURCES:
         name = os.path.basename(src)
         obj = os.path.join(OBJDIR, name + ".o")
         cmd = ([cc] + HIP_FLAGS + PER_SOURCE_FLAGS.get(name, []) +
                ["-I" + INCLUDE, "-I" + CSRC, "-c", src, "-o", obj])
         if verbose:
             print(" ".join(cmd), flush=True)
-        jobs.append((name, obj, subprocess.Popen(cmd, stdout=subprocess.PIPE,
-                                                 stderr=subprocess.STDOUT, text=True)))
+        jobs.append((src, obj, subprocess.Popen(cmd, stdout=subprocess.PIPE,
+                                                stderr=subprocess.STDOUT, text=True)))
     failed = []
-    for name, _, proc in jobs:
+    for src, _, proc in jobs:
         out, _ = proc.communicate()
         if proc.returncode != 0:
             sys.stderr.write(out)
-            failed.append(name)
+            failed.append(os.path.basename(src))
     if failed:
         raise RuntimeError("hipcc failed compiling " + ", ".join(failed))
-    cmd = [cc] + LINK_FLAGS + ["-o", LIB + ".tmp"] + [obj for _, obj, _ in jobs]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed linking libattn_dense.so")
-    os.replace(LIB + ".tmp", LIB)
+    objs = {src: obj for src, obj, _ in jobs}
+    for lib, sources in ((LIB, SOURCES), (PROBE_LIB, PROBE_SOURCES)):
+        cmd = [cc] + LINK_FLAGS + ["-o", lib + ".tmp"] + [objs[s] for s in sources]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            sys.stderr.write(res.stdout + res.stderr)
+            raise RuntimeError(f"hipcc failed linking {os.path.basename(lib)}")
+        os.replace(lib + ".tmp", lib)
     return LIB
 
 

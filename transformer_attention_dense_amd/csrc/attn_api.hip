@@ -9,6 +9,7 @@
 #include <stdlib.h>
 
 #include <mutex>
+#include <vector>
 
 #include "attn_dense.h"
 #include "attn_launch.h"
@@ -18,13 +19,22 @@ namespace {
 constexpr int kMaxDevices = 64;
 constexpr long long kIndexLimit = (1LL << 31) - 1;
 
+// Split-KV (and block-causal id summary) work space of one device. The library's own
+// buffer only grows; a superseded buffer is never freed, because launches already
+// enqueued on any stream and HIP graphs captured earlier may still use it (it is
+// released with the process). A caller-supplied buffer (attn_set_workspace) takes
+// precedence and is never grown.
 struct Workspace {
     void* ptr = nullptr;
     size_t bytes = 0;
+    std::vector<void*> retired;
+    void* user = nullptr;
+    size_t user_bytes = 0;
 };
 
 std::mutex g_ws_mutex;
 Workspace g_ws[kMaxDevices];
+constexpr size_t kWsGranule = 2u << 20;  // growth is rounded up to 2 MiB
 
 struct Plan {
     int splits;
@@ -80,9 +90,10 @@ int make_plan(int B, int Nq, int Nk, int H, int D, int num_splits, int waves, Pl
 
     int s = num_splits;
     if (s == 0) {
-        // Split the keys only when the grid underfills the GPU (256 CUs, two
-        // workgroups each) and every split keeps at least four key tiles.
-        const long long target = 512;
+        // Split the keys only when the grid underfills the GPU and every split keeps
+        // at least four key tiles. The GPU holds one 8-wave workgroup per CU (96 KiB of
+        // LDS, two waves per SIMD) and two of the 2- and 4-wave ones: 256 CUs x that.
+        const long long target = (w == 8) ? 256 : 512;
         s = 1;
         while (base * s * 2 <= target && key_tiles / (s * 2) >= 4) s *= 2;
     }
@@ -103,40 +114,69 @@ int make_plan(int B, int Nq, int Nk, int H, int D, int num_splits, int waves, Pl
     return ATTN_OK;
 }
 
+int current_device(int* dev) {
+    if (hipGetDevice(dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return ATTN_ERR_HIP;
+    }
+    if (*dev < 0 || *dev >= kMaxDevices) return ATTN_ERR_WORKSPACE;
+    return ATTN_OK;
+}
+
+// Returns in *ptr_out a work space of at least `bytes` on the current device: the
+// caller's buffer when one is set (ATTN_ERR_WORKSPACE if it is too small), else the
+// library's, grown if needed. The pointer stays valid until the process ends (or, for
+// a caller's buffer, as long as the caller keeps it).
 int reserve(long long bytes, void** ptr_out) {
     if (bytes <= 0) {
         if (ptr_out) *ptr_out = nullptr;
         return ATTN_OK;
     }
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return ATTN_ERR_HIP;
-    if (dev < 0 || dev >= kMaxDevices) return ATTN_ERR_WORKSPACE;
+    const int drc = current_device(&dev);
+    if (drc != ATTN_OK) return drc;
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     Workspace& ws = g_ws[dev];
+    if (ws.user) {
+        if (ws.user_bytes < (size_t)bytes) return ATTN_ERR_WORKSPACE;
+        if (ptr_out) *ptr_out = ws.user;
+        return ATTN_OK;
+    }
     if (ws.bytes < (size_t)bytes) {
+        // Fault injection for tests: behave as if the allocation failed.
         if (getenv("ATTN_TEST_FAIL_ALLOC")) return ATTN_ERR_WORKSPACE;
-        if (ws.ptr) {
-            // Earlier launches may still read the old buffer.
-            if (hipDeviceSynchronize() != hipSuccess) return ATTN_ERR_HIP;
-            (void)hipFree(ws.ptr);
-            ws.ptr = nullptr;
-            ws.bytes = 0;
-        }
+        size_t want = (size_t)bytes > 2 * ws.bytes ? (size_t)bytes : 2 * ws.bytes;
+        want = (want + kWsGranule - 1) / kWsGranule * kWsGranule;
         void* p = nullptr;
-        if (hipMalloc(&p, (size_t)bytes) != hipSuccess || !p) {
+        if (hipMalloc(&p, want) != hipSuccess || !p) {
             (void)hipGetLastError();
-            return ATTN_ERR_WORKSPACE;
+            p = nullptr;
+            want = (size_t)bytes;  // the doubling may be what did not fit
+            if (hipMalloc(&p, want) != hipSuccess || !p) {
+                (void)hipGetLastError();
+                return ATTN_ERR_WORKSPACE;
+            }
         }
+        if (ws.ptr) ws.retired.push_back(ws.ptr);
         ws.ptr = p;
-        ws.bytes = (size_t)bytes;
+        ws.bytes = want;
     }
     if (ptr_out) *ptr_out = ws.ptr;
     return ATTN_OK;
 }
 
-int run(const void* q, const void* k0, const void* v0, int n0, const void* k1, const void* v1,
-        int n1, void* out, int B, int Nq, int H, int D, int num_splits, int waves,
-        void* stream) {
+}  // namespace
+
+namespace attn {
+
+// The dense / prefix / cross forward behind every entry point. `fixed` (may be null)
+// is a work space handed in for this call only; without it the device's work space
+// (reserve) is used when the plan splits the keys.
+__attribute__((visibility("hidden"))) int run_fwd(const void* q, const void* k0, const void* v0,
+                                                  int n0, const void* k1, const void* v1, int n1,
+                                                  void* out, int B, int Nq, int H, int D,
+                                                  int num_splits, int waves, void* stream,
+                                                  const FixedWorkspace* fixed) {
     if (!q || !out) return ATTN_ERR_NULL;
     if (n0 < 0 || n1 < 0) return ATTN_ERR_SHAPE;
     if (n0 > 0 && (!k0 || !v0)) return ATTN_ERR_NULL;
@@ -160,8 +200,19 @@ int run(const void* q, const void* k0, const void* v0, int n0, const void* k1, c
     // ---- device work from here on
     void* ws = nullptr;
     if (plan.splits > 1) {
-        const int wrc = reserve(plan.workspace_bytes, &ws);
-        if (wrc != ATTN_OK) return wrc;
+        if (fixed) {
+            if (!fixed->ptr || fixed->bytes < plan.workspace_bytes) return ATTN_ERR_WORKSPACE;
+            ws = fixed->ptr;
+        } else {
+            const int wrc = reserve(plan.workspace_bytes, &ws);
+            if (wrc != ATTN_OK) return wrc;
+        }
+        // a caller's work space must not overlap the tensors of the call
+        const long long wb = plan.workspace_bytes;
+        if (overlaps(ws, wb, out, qbytes) || overlaps(ws, wb, q, qbytes) ||
+            overlaps(ws, wb, k0, s0) || overlaps(ws, wb, v0, s0) || overlaps(ws, wb, k1, s1) ||
+            overlaps(ws, wb, v1, s1))
+            return ATTN_ERR_ALIAS;
     }
     const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     attn::FwdParams p;
@@ -205,6 +256,12 @@ int run(const void* q, const void* k0, const void* v0, int n0, const void* k1, c
     return ATTN_OK;
 }
 
+}  // namespace attn
+
+namespace {
+
+using attn::run_fwd;
+
 // Block-causal attention without prefix: keys are the queries' own positions.
 int run_block_causal(const void* q, const void* k, const void* v, const int* ids, void* out,
                      int B, int N, int H, int D, void* stream) {
@@ -225,6 +282,10 @@ int run_block_causal(const void* q, const void* k, const void* v, const int* ids
     void* ws = nullptr;
     const int wrc = reserve(nblk * 16, &ws);
     if (wrc != ATTN_OK) return wrc;
+    if (overlaps(ws, nblk * 16, out, bytes) || overlaps(ws, nblk * 16, q, bytes) ||
+        overlaps(ws, nblk * 16, k, bytes) || overlaps(ws, nblk * 16, v, bytes) ||
+        overlaps(ws, nblk * 16, ids, idbytes))
+        return ATTN_ERR_ALIAS;
     const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     attn::FwdParams p;
     p.q = static_cast<const uint16_t*>(q);
@@ -317,27 +378,28 @@ int attn_na3d(const void* q, const void* k, const void* v, void* out, int B, int
 int attn_dense(const void* q, const void* k, const void* v, void* out, int B, int N, int H,
                int D, void* stream) {
     if (N < 1) return ATTN_ERR_SHAPE;
-    return run(q, k, v, N, nullptr, nullptr, 0, out, B, N, H, D, 0, 0, stream);
+    return run_fwd(q, k, v, N, nullptr, nullptr, 0, out, B, N, H, D, 0, 0, stream, nullptr);
 }
 
 int attn_prefix(const void* q, const void* kp, const void* vp, const void* kc, const void* vc,
                 void* out, int B, int Nq, int Np, int H, int D, void* stream) {
     if (Np < 0 || Nq < 1) return ATTN_ERR_SHAPE;
     if (!kc || !vc) return ATTN_ERR_NULL;
-    return run(q, kp, vp, Np, kc, vc, Nq, out, B, Nq, H, D, 0, 0, stream);
+    return run_fwd(q, kp, vp, Np, kc, vc, Nq, out, B, Nq, H, D, 0, 0, stream, nullptr);
 }
 
 int attn_cross(const void* q, const void* k, const void* v, void* out, int B, int Nq, int Nk,
                int H, int D, void* stream) {
     if (Nk < 1) return ATTN_ERR_SHAPE;
-    return run(q, k, v, Nk, nullptr, nullptr, 0, out, B, Nq, H, D, 0, 0, stream);
+    return run_fwd(q, k, v, Nk, nullptr, nullptr, 0, out, B, Nq, H, D, 0, 0, stream, nullptr);
 }
 
 int attn_fwd_ex(const void* q, const void* k0, const void* v0, int n0, const void* k1,
                 const void* v1, int n1, void* out, int B, int Nq, int H, int D, int num_splits,
                 int waves, void* stream) {
     if ((long long)n0 + n1 < 1) return ATTN_ERR_SHAPE;
-    return run(q, k0, v0, n0, k1, v1, n1, out, B, Nq, H, D, num_splits, waves, stream);
+    return run_fwd(q, k0, v0, n0, k1, v1, n1, out, B, Nq, H, D, num_splits, waves, stream,
+                   nullptr);
 }
 
 int attn_plan(int B, int Nq, int Nk, int H, int D, int num_splits, int waves, int* splits,
@@ -364,6 +426,18 @@ int attn_na3d_plan(int B, int T, int Y, int X, int H, int D, int kt, int ky, int
 
 int attn_reserve_workspace(long long bytes) { return reserve(bytes, nullptr); }
 
+int attn_set_workspace(void* ptr, long long bytes) {
+    if (ptr && bytes < 0) return ATTN_ERR_SHAPE;
+    if ((reinterpret_cast<uintptr_t>(ptr) & 255u) != 0) return ATTN_ERR_ALIGN;
+    int dev = 0;
+    const int drc = current_device(&dev);
+    if (drc != ATTN_OK) return drc;
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    g_ws[dev].user = ptr;
+    g_ws[dev].user_bytes = ptr ? (size_t)bytes : 0;
+    return ATTN_OK;
+}
+
 const char* attn_strerror(int code) {
     switch (code) {
         case ATTN_OK: return "success";
@@ -371,9 +445,10 @@ const char* attn_strerror(int code) {
         case ATTN_ERR_SHAPE: return "a batch, sequence or head count is out of range";
         case ATTN_ERR_UNSUPPORTED: return "unsupported head dimension or launch option";
         case ATTN_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
-        case ATTN_ERR_ALIAS: return "the output overlaps an input";
+        case ATTN_ERR_ALIAS: return "the output or the caller's work space overlaps an input";
         case ATTN_ERR_OVERFLOW: return "a size exceeds the kernels' index range";
-        case ATTN_ERR_WORKSPACE: return "the split-KV work space could not be allocated";
+        case ATTN_ERR_WORKSPACE:
+            return "the work space could not be allocated or the caller's is too small";
         case ATTN_ERR_HIP: return "a HIP runtime call or kernel launch failed";
         default: return "unknown error code";
     }

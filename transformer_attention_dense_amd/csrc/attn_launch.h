@@ -60,6 +60,20 @@ void na3d_configure(NaParams& p);
 long long na3d_workgroups(const NaParams& p);
 hipError_t launch_na3d(const NaParams& p, hipStream_t stream);
 
+// A work space handed to one forward call (instead of the device's shared one).
+struct FixedWorkspace {
+    void* ptr;
+    long long bytes;
+};
+
+// The dense / prefix / cross forward behind the C entry points (attn_api.hip): checks
+// the arguments, plans the launch and enqueues the kernels. Returns ATTN_OK or an
+// ATTN_ERR_* code. With `fixed` null the split-KV work space is the device's shared
+// one; otherwise `fixed` must hold the plan's work space (else ATTN_ERR_WORKSPACE).
+int run_fwd(const void* q, const void* k0, const void* v0, int n0, const void* k1,
+            const void* v1, int n1, void* out, int B, int Nq, int H, int D, int num_splits,
+            int waves, void* stream, const FixedWorkspace* fixed);
+
 // Keys per tile of the forward kernels; split ranges are multiples of it.
 constexpr int kKeyTile = 64;
 
