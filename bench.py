@@ -190,24 +190,53 @@ def probe_library():
     return lib
 
 
-def enqueue_clock_probe(torch, stream, workgroups=256, ticks=2000):
-    """Enqueues the clock probe on `stream` (behind the launches already there); returns
-    a function giving the median shader clock in GHz once the stream has run it."""
-    lib = probe_library()
-    if lib is None:
-        return lambda: None
-    buf = torch.zeros(workgroups, dtype=torch.float32, device="cuda")
-    if lib.attn_probe_clock(buf.data_ptr(), workgroups, ticks, stream.cuda_stream) != 0:
-        return lambda: None
-    mhz = lib.attn_probe_realtime_mhz()
+class ClockProbe:
+    """The shader-clock probe (libattn_probe.so). Created before the warmup, so its code
+    is loaded on the GPU before anything is measured."""
 
-    def read():
-        v = buf.cpu()
-        v = v[v > 0]
-        if v.numel() == 0 or mhz <= 0:
+    def __init__(self, torch, workgroups=256, ticks=2000):
+        self.lib = probe_library()
+        self.torch = torch
+        self.workgroups = workgroups
+        self.ticks = ticks
+        self.mhz = self.lib.attn_probe_realtime_mhz() if self.lib else 0.0
+        if self.lib is not None:
+            self.measure_now(torch.cuda.current_stream())  # load the module
+
+    def enqueue(self, stream):
+        """Enqueues one probe behind the launches already on `stream`; returns its output
+        buffer (read it after the stream has run)."""
+        buf = self.torch.zeros(self.workgroups, dtype=self.torch.float32, device="cuda")
+        rc = self.lib.attn_probe_clock(buf.data_ptr(), self.workgroups, self.ticks,
+                                       stream.cuda_stream)
+        return buf if rc == 0 else None
+
+    def ghz(self, bufs):
+        """Median shader clock in GHz over the probes' workgroups (None if unknown)."""
+        vals = [b.cpu() for b in bufs if b is not None]
+        if not vals or self.mhz <= 0:
             return None
-        return round(float(v.median()) * mhz / 1000.0, 3)
-    return read
+        v = self.torch.cat(vals)
+        v = v[v > 0]
+        return round(float(v.median()) * self.mhz / 1000.0, 3) if v.numel() else None
+
+    def measure_now(self, stream):
+        buf = self.enqueue(stream)
+        self.torch.cuda.synchronize()
+        return self.ghz([buf])
+
+    def under_load(self, call, stream, rounds=4, steps=50):
+        """Clock under the workload itself, outside any timed region: `rounds` times,
+        `steps` more calls followed by one probe on the same stream."""
+        if self.lib is None:
+            return None
+        bufs = []
+        for _ in range(rounds):
+            for _ in range(steps):
+                call()
+            bufs.append(self.enqueue(stream))
+        self.torch.cuda.synchronize()
+        return self.ghz(bufs)
 
 
 def environment(torch):
@@ -278,6 +307,8 @@ def bench_one(w, steps, warmup, warmup_seconds, torch, attn, ts):
         dts = [to_device(t, torch) for t in ts]
     out, call = make_call(w, dts, attn)
     stream = torch.cuda.current_stream()
+    probe = ClockProbe(torch)
+    clock_idle = probe.measure_now(stream) if probe.lib else None
     # warmup: at least `warmup` steps and at least `warmup_seconds` of them
     torch.cuda.synchronize()
     w0 = time.perf_counter()
@@ -296,12 +327,11 @@ def bench_one(w, steps, warmup, warmup_seconds, torch, attn, ts):
     for _ in range(steps):
         call()
     ev1.record(stream)
-    clock = enqueue_clock_probe(torch, stream)  # right behind the timed launches
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ev_ms = ev0.elapsed_time(ev1)
-    clock_ghz = clock()
     timed_out = device_bits(out, torch)  # the output the timed steps wrote
+    clock_ghz = probe.under_load(call, stream)
     inputs_unchanged = all(np.array_equal(device_bits(d, torch), np.ascontiguousarray(t))
                            for d, t in zip(dts, ts))
     # per-call event timing (the pages' eager method: median of event-bracketed calls)
@@ -329,7 +359,7 @@ def bench_one(w, steps, warmup, warmup_seconds, torch, attn, ts):
     graph = graph_timing(torch, call, out)
     return {"wall_s": wall, "event_ms": ev_ms, "median_call_us": statistics.median(samples),
             "plan": plan, "finite": finite, "graph": graph, "warm": warm,
-            "clock_ghz": clock_ghz, "timed_out": timed_out,
+            "clock_ghz": clock_ghz, "clock_idle_ghz": clock_idle, "timed_out": timed_out,
             "inputs_unchanged": inputs_unchanged}
 
 
@@ -391,7 +421,10 @@ def record(w, r, steps, warmup, cpu, check, env):
             "algorithmic_bytes_per_launch": w.algorithmic_bytes,
             "hbm_gbs_algorithmic": round(w.algorithmic_bytes / (launch_us * 1e-6) / 1e9, 1),
         },
-        "clock_ghz_after_timed_steps": r["clock_ghz"],
+        # shader clock (s_memtime cycles per s_memrealtime tick) from probes enqueued
+        # behind 4 x 50 more steps after the timed ones, and before the warmup (idle)
+        "clock_ghz_under_load": r["clock_ghz"],
+        "clock_ghz_idle": r["clock_idle_ghz"],
         "outputs_finite": r["finite"],
         "inputs_unchanged": r["inputs_unchanged"],
     }

@@ -437,8 +437,10 @@ def test_caller_work_space_used_and_checked():
         with pytest.raises(attn.AttnError) as e:
             attn.fwd_ex(tq, tk, tv, num_splits=3)
         assert e.value.code == -7
+        # an output that starts 256 bytes before the end of the work space the call uses
         big = torch.empty(need + tq.numel() * 2 + 4096, dtype=torch.uint8, device="cuda")
-        outv = big[-tq.numel() * 2:].view(torch.bfloat16).view(tq.shape)
+        off = (need // 256) * 256 - 256
+        outv = big[off:off + tq.numel() * 2].view(torch.bfloat16).view(tq.shape)
         attn.set_workspace(big)
         with pytest.raises(attn.AttnError) as e:
             attn.fwd_ex(tq, tk, tv, out=outv, num_splits=3)
