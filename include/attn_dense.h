@@ -140,6 +140,22 @@ int attn_fwd_ex(const void* q, const void* k0, const void* v0, int n0, const voi
                 int waves, void* stream);
 
 /*
+ * attn_fwd_ex without any allocation, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments, results and errors as attn_fwd_ex, except for the split-KV work
+ * space: it is a static device array of 64 MiB (67108864 bytes) that the library holds
+ * on every GPU it runs on until the process ends, never the library's or the caller's
+ * work space above. A plan that needs more (attn_plan's workspace_bytes) returns
+ * ATTN_ERR_WORKSPACE before any work is enqueued. Every call on one GPU shares that
+ * array: calls that may overlap in time on one GPU (different streams, or graphs
+ * replayed concurrently) race and must be ordered by the caller. No call here
+ * allocates, frees or synchronises.
+ */
+int attn_fwd_ex_noalloc(const void* q, const void* k0, const void* v0, int n0, const void* k1,
+                        const void* v1, int n1, void* out, int B, int Nq, int H, int D,
+                        int num_splits, int waves, void* stream);
+
+/*
  * Launch plan the library would use for a call, computed on the host only (no HIP
  * call). Any output pointer may be NULL. Returns ATTN_OK or a shape/size error.
  *   splits:          key ranges computed in parallel (1 = no combine step)

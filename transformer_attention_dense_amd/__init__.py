@@ -7,6 +7,7 @@ library is missing or fails to load, importing the low-level functions raises.
 Low-level functions (same names and arguments as the C ABI; tensors passed as raw
 device addresses, ``stream`` as an integer hipStream_t):
     attn_dense, attn_prefix, attn_cross, attn_block_causal, attn_na3d, attn_fwd_ex,
+    attn_fwd_ex_noalloc,
     attn_plan, attn_na3d_plan, attn_reserve_workspace, attn_set_workspace, attn_strerror,
     attn_abi_version
 
@@ -37,7 +38,7 @@ ERRORS = {
 
 # Exported symbols, in header order.
 SYMBOLS = ("attn_dense", "attn_prefix", "attn_cross", "attn_block_causal", "attn_na3d",
-           "attn_fwd_ex",
+           "attn_fwd_ex", "attn_fwd_ex_noalloc",
            "attn_plan", "attn_na3d_plan", "attn_reserve_workspace", "attn_set_workspace",
            "attn_strerror", "attn_abi_version")
 
@@ -67,6 +68,7 @@ def library() -> ctypes.CDLL:
     lib.attn_block_causal.argtypes = [p, p, p, p, p, i, i, i, i, p]
     lib.attn_na3d.argtypes = [p, p, p, p] + [i] * 9 + [p]
     lib.attn_fwd_ex.argtypes = [p, p, p, i, p, p, i, p, i, i, i, i, i, i, p]
+    lib.attn_fwd_ex_noalloc.argtypes = [p, p, p, i, p, p, i, p, i, i, i, i, i, i, p]
     lib.attn_plan.argtypes = [i, i, i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i),
                               ctypes.POINTER(ll), ctypes.POINTER(ll)]
     lib.attn_na3d_plan.argtypes = [i] * 9 + [ctypes.POINTER(i), ctypes.POINTER(ll)]
@@ -108,6 +110,12 @@ def attn_fwd_ex(q, k0, v0, n0, k1, v1, n1, out, B, Nq, H, D, num_splits=0, waves
                 stream=0) -> int:
     return library().attn_fwd_ex(q, k0, v0, n0, k1, v1, n1, out, B, Nq, H, D, num_splits,
                                  waves, stream)
+
+
+def attn_fwd_ex_noalloc(q, k0, v0, n0, k1, v1, n1, out, B, Nq, H, D, num_splits=0, waves=0,
+                        stream=0) -> int:
+    return library().attn_fwd_ex_noalloc(q, k0, v0, n0, k1, v1, n1, out, B, Nq, H, D,
+                                         num_splits, waves, stream)
 
 
 def attn_na3d_plan(B, T, Y, X, H, D, kt, ky, kx):

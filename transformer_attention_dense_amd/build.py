@@ -17,7 +17,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn_dense.so")
 OBJDIR = os.path.join(PKG, "_build")
 SOURCES = [os.path.join(CSRC, "attn_kernels.hip"), os.path.join(CSRC, "attn_pingpong.hip"),
-           os.path.join(CSRC, "attn_na3d.hip"), os.path.join(CSRC, "attn_api.hip")]
+           os.path.join(CSRC, "attn_na3d.hip"), os.path.join(CSRC, "attn_api.hip"),
+           os.path.join(CSRC, "attn_noalloc.hip")]
 PROBE_LIB = os.path.join(PKG, "libattn_probe.so")
 PROBE_SOURCES = [os.path.join(CSRC, "attn_probe.hip")]
 
