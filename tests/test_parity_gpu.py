@@ -104,6 +104,25 @@ def test_outlier_logits_small():
                         f"outliers s{splits} w{waves}")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("splits,waves", [(1, 8), (1, 4), (2, 8)])
+def test_logits_growing_along_the_keys(D, splits, waves):
+    """Later keys carry logits far above the first tile's (the last 100 keys x6, then
+    x12 on the last 20): the running reference of the first tile is no longer close
+    enough, so the tiles are redone against their own maximum, and the rows that needed
+    it stay on that path."""
+    B, N, H = 1, 700, 3
+    w = synth.small("dense", B, N, H, D, 650 + D, sigma_qk=1.0)
+    q, k, v = w.tensors()
+    kf = synth.bf16_bits_to_f32(k).copy()
+    kf[:, -100:] *= 6.0
+    kf[:, -20:] *= 2.0
+    k = synth.f32_to_bf16_bits(kf)
+    say(f"growing logits D{D} splits{splits} waves{waves}")
+    assert_accepted(run_ex(q, k, v, splits=splits, waves=waves), oracle.attention(q, k, v),
+                    f"growing logits D{D} s{splits} w{waves}")
+
+
 # ---------------------------------------------------------------- block-causal, every element
 
 def ids_from(segments):
