@@ -23,6 +23,13 @@ typedef __attribute__((address_space(3))) uint16_t lds_u16;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr float kRescaleLog2 = 8.0f;
+// Largest sum of one lane's probabilities of a tile that is accepted without computing
+// the tile's row maximum (lazy softmax): every probability is then at most 2^64, and a
+// row's output accumulates at most (keys) * 2^64 * |V|, far inside FP32 range; BF16
+// probabilities keep their relative precision at any magnitude.
+constexpr float kLazySumLimit = 18446744073709551616.0f;  // 2^64
+// Largest |running reference| (scaled logits, log2 units) of rows that go lazy.
+constexpr float kLazyRefLog2 = 40.0f;
 constexpr int kWave = 64;
 
 __device__ __forceinline__ float wave_swap_max(float x) {

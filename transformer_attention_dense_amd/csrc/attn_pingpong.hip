@@ -239,6 +239,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     f32x16 s[NB];       // scores of the tile between its G and S phases
     bf16x8 pf[NB][2];   // probabilities of the tile between its S and next G phases
     float m_ref = -INFINITY;
+    float mc_ref = 0.f;        // m_ref * c (0 while m_ref is -inf)
+    bool lazy_ok = false;      // wave-uniform: the next tile may skip its row maximum
+    bool eager_rows = false;   // wave-uniform: these rows stay on the row-maximum path
     float l_part = 0.f;
     const float c = p.c;
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
@@ -367,6 +370,32 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     if (key >= kend) s[kb][r] = -INFINITY;
                 }
         }
+        if (lazy_ok) {
+            // Lazy tile (every tile after the rows' first): probabilities against the
+            // running reference m_ref, without the tile's row maximum. The lane's sum of
+            // its probabilities bounds each of them; if no sum exceeds kLazySumLimit and
+            // all are finite, the tile is done (the reference may lag the true maximum:
+            // O and l share it, so O / l is unchanged). Otherwise the tile is redone
+            // below against its own maximum, as is every later tile of these rows.
+            float l2[2] = {0.f, 0.f};
+            static_for<NPAIR>([&](auto pc) {
+                constexpr int pi = decltype(pc)::value;
+                constexpr int cc = pi / 4, kb = cc / 2, tt = cc % 2, r = 8 * tt + 2 * (pi % 4);
+                const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -mc_ref));
+                const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r + 1], c, -mc_ref));
+                const bf16x2 pk = {(__bf16)e0, (__bf16)e1};
+                l2[pi % 2] = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, l2[pi % 2], false);
+                pf[kb][tt][r & 7] = pk[0];
+                pf[kb][tt][(r & 7) + 1] = pk[1];
+            });
+            const float ls = l2[0] + l2[1];
+            if (__builtin_amdgcn_ballot_w64(!(ls <= kLazySumLimit)) == 0) {
+                l_part += ls;
+                return;
+            }
+            lazy_ok = false;  // redo this tile, and every later one of these rows, eagerly
+            eager_rows = true;
+        }
         // row maximum: four independent chains of EPC consecutive registers, then one
         // exchange with lane ^ 32
         constexpr int EPC = NB * 4;
@@ -388,8 +417,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
             for (int i = 0; i < DB; ++i) o[i] *= alpha;
             m_ref = m_new;
+            mc_ref = (m_ref == -INFINITY) ? 0.f : m_ref * c;
         }
-        const float mc = (m_ref == -INFINITY) ? 0.f : m_ref * c;
+        const float mc = mc_ref;
         float l2[2] = {0.f, 0.f};
         static_for<NPAIR>([&](auto pc) {
             constexpr int pi = decltype(pc)::value;
@@ -402,6 +432,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             pf[kb][tt][(r & 7) + 1] = pk[1];
         });
         l_part += l2[0] + l2[1];
+        // After the rows' first tile: the later tiles go lazy when every row has a finite
+        // reference of moderate size. Rows whose logits reach beyond 2^kLazyRefLog2 tend
+        // to keep growing past kLazySumLimit, so they stay on this path for good.
+        if (!eager_rows) {
+            eager_rows = __builtin_amdgcn_ballot_w64(
+                             !(m_ref > -INFINITY && fabsf(mc_ref) <= kLazyRefLog2)) != 0;
+            lazy_ok = !eager_rows;
+        }
     };
 
     using TRUE_ = std::true_type;
