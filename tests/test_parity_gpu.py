@@ -123,6 +123,33 @@ def test_logits_growing_along_the_keys(D, splits, waves):
                     f"growing logits D{D} s{splits} w{waves}")
 
 
+# ---------------------------------------------------------------- short sequences
+
+@pytest.mark.parametrize("B,Nq,Nk,H", [(100, 50, 37, 32), (97, 64, 64, 32), (3, 1, 5, 7),
+                                       (130, 33, 64, 24), (2, 64, 1, 3)])
+def test_short_sequences_every_element(B, Nq, Nk, H):
+    """At most 64 query rows and keys per (batch, head) at D = 64, many (batch, head)
+    pairs: one key tile per two-wave workgroup; ragged row and key counts, one wave idle
+    when Nq <= 32."""
+    D = 64
+    plan = attn.attn_plan(B, Nq, Nk, H, D)
+    assert plan["splits"] == 1 and plan["waves"] == 2
+    say(f"short B{B} Nq{Nq} Nk{Nk} H{H}: {plan}")
+    w = synth.small("dense", B, Nq, H, D, 1800 + Nq + Nk, Nk=Nk, sigma_qk=2.0)
+    q, k, v = w.tensors()
+    got = host(attn.cross(dev(q), dev(k), dev(v)) if Nq != Nk else attn.dense(dev(q), dev(k), dev(v)))
+    assert_accepted(got, oracle.attention(q, k, v), f"short B{B} Nq{Nq} Nk{Nk} H{H}")
+
+
+def test_short_prefix_keys_from_both_segments():
+    """Prefix-cached call whose prefix and current keys together fit in one short tile."""
+    B, Nq, Np, H, D = 100, 40, 20, 32, 64
+    w = synth.small("prefix", B, Nq, H, D, 1850, Np=Np, sigma_qk=2.0)
+    q, kp, vp, kc, vc = w.tensors()
+    got = host(attn.prefix(dev(q), dev(kp), dev(vp), dev(kc), dev(vc)))
+    assert_accepted(got, oracle.prefix_attention(q, kp, vp, kc, vc), "short prefix")
+
+
 # ---------------------------------------------------------------- block-causal, every element
 
 def ids_from(segments):
