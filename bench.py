@@ -265,6 +265,28 @@ def environment(torch):
     return env
 
 
+def stream_bandwidth(torch, mib=512, reps=20):
+    """Achievable HBM bandwidth on this machine for reference: a plain streaming kernel
+    (torch.neg on float32, reads and writes `mib` MiB each), median of `reps` event-timed
+    calls after a warmup, in GB/s of bytes read plus written."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.neg(src, out=dst)
+    times = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        torch.neg(src, out=dst)
+        b.record()
+        b.synchronize()
+        times.append(a.elapsed_time(b) / 1000.0)
+    del src, dst
+    return round(2 * mib * (1 << 20) / statistics.median(times) / 1e9, 1)
+
+
 def graph_timing(torch, call, out):
     """The pages' graph mode: 20 calls captured in one HIP graph (torch's capture of the
     current stream), replayed 10 times; median microseconds per call. The output after
@@ -357,9 +379,11 @@ def bench_one(w, steps, warmup, warmup_seconds, torch, attn, ts):
         plan = attn.attn_plan(w.B, w.Nq, w.keys, w.H, w.D)
     finite = bool(torch.isfinite(out.float()).all())
     graph = graph_timing(torch, call, out)
+    stream_gbs = stream_bandwidth(torch) if w.flop / w.algorithmic_bytes < 315 else None
     return {"wall_s": wall, "event_ms": ev_ms, "median_call_us": statistics.median(samples),
             "plan": plan, "finite": finite, "graph": graph, "warm": warm,
             "clock_ghz": clock_ghz, "clock_idle_ghz": clock_idle, "timed_out": timed_out,
+            "stream_gbs": stream_gbs,
             "inputs_unchanged": inputs_unchanged}
 
 
@@ -433,6 +457,8 @@ def record(w, r, steps, warmup, cpu, check, env):
                                 "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                 "frac": round(rec["roofline"]["hbm_gbs_algorithmic"]
                                               / PEAK_HBM_GBS, 4)})
+        if r.get("stream_gbs"):
+            rec["roofline"]["stream_copy_gbs_this_box"] = r["stream_gbs"]
     mf = stored.get("mfma")
     if mf and rec["roofline"]["bound"] == "mfma" and mf["profiled_duration_us"] >= 100:
         # Not measured in this run: from a separate, committed counter run of the same
