@@ -52,6 +52,7 @@ SHARED_SOURCES = ["attn_device.h", "attn_api.hip", "attn_launch.h", "../build.py
 KIND_SOURCES = {"na3d": ["attn_na3d.hip"]}
 DENSE_SOURCES = ["attn_kernels.hip", "attn_pingpong.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+CALIBRATING = False  # set by --calib-mib
 
 
 def kernel_source_hash(kind) -> str:
@@ -379,7 +380,9 @@ def bench_one(w, steps, warmup, warmup_seconds, torch, attn, ts):
         plan = attn.attn_plan(w.B, w.Nq, w.keys, w.H, w.D)
     finite = bool(torch.isfinite(out.float()).all())
     graph = graph_timing(torch, call, out)
-    stream_gbs = stream_bandwidth(torch) if w.flop / w.algorithmic_bytes < 315 else None
+    # (not in counter-calibration runs: those scale by the torch.neg dispatches they see)
+    stream_gbs = (stream_bandwidth(torch)
+                  if w.flop / w.algorithmic_bytes < 315 and not CALIBRATING else None)
     return {"wall_s": wall, "event_ms": ev_ms, "median_call_us": statistics.median(samples),
             "plan": plan, "finite": finite, "graph": graph, "warm": warm,
             "clock_ghz": clock_ghz, "clock_idle_ghz": clock_idle, "timed_out": timed_out,
@@ -628,6 +631,8 @@ def main():
     attn.library()  # fail loudly if the HIP library is missing
 
     if args.calib_mib:
+        global CALIBRATING
+        CALIBRATING = True
         n = args.calib_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)

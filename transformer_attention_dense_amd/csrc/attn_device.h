@@ -45,25 +45,37 @@ __device__ __forceinline__ float wave_swap_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Workgroups one XCD holds at once for the 8-wave kernels: one per CU, 32 CUs per XCD.
+constexpr int kXcdSlots = 32;
+
 // Workgroup -> (query block, batch*head, split). Workgroups are dispatched to the
 // 8 XCDs round-robin by linear id; this remap gives each XCD a contiguous range of
 // (query block, head) work so the query blocks sharing one head's K/V run on the same
 // XCD and hit its L2.
 //
-// heavy_last_blocks (causal-like masks, where later query blocks see more keys): within
-// each XCD's share, hand out query blocks from the last to the first, cycling over the
-// share's heads, so the longest workgroups start first (the share keeps its heads, so
-// their K/V stay in that XCD's L2).
+// heavy_last_blocks (causal-like masks, where later query blocks see more keys): the
+// XCD's share of heads is cut into groups of heads whose blocks together fill the XCD's
+// workgroup slots (slots_per_xcd); within a group, query blocks are handed out from the
+// last to the first, cycling over the group's heads, so the longest workgroups start
+// first. The first group's blocks all start together and read each K/V tile of a head
+// at nearly the same time; a later group's light blocks start while its heavy blocks
+// still run, so they find the first K/V tiles in the XCD's L2 more often than when the
+// heavy blocks of every head in the share go first.
 __device__ __forceinline__ void decode_workgroup(int m_blocks, int bh_count, int& mb, int& bh,
-                                                 int& split, bool heavy_last_blocks = false) {
+                                                 int& split, bool heavy_last_blocks = false,
+                                                 int slots_per_xcd = kXcdSlots) {
     const int L = blockIdx.x;
     const int T = gridDim.x;
     const int per = T >> 3;
     int L2 = (L < (per << 3)) ? (L & 7) * per + (L >> 3) : L;
     if (heavy_last_blocks && L < (per << 3) && per % m_blocks == 0) {
         const int hx = per / m_blocks;  // heads in this XCD's share
+        const int g = max(1, min(hx, slots_per_xcd / m_blocks));  // heads per group
         const int r = L2 % per;
-        L2 = (L2 - r) + (r % hx) * m_blocks + (m_blocks - 1 - r / hx);
+        const int h0 = (r / (g * m_blocks)) * g;  // first head of r's group
+        const int gn = min(g, hx - h0);           // heads in r's group
+        const int q = r - h0 * m_blocks;          // position inside the group
+        L2 = (L2 - r) + (h0 + q % gn) * m_blocks + (m_blocks - 1 - q / gn);
     } else if (heavy_last_blocks) {
         L2 = (L2 / m_blocks) * m_blocks + (m_blocks - 1 - L2 % m_blocks);
     }
