@@ -125,13 +125,13 @@ def test_logits_growing_along_the_keys(D, splits, waves):
 
 # ---------------------------------------------------------------- short sequences
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("B,Nq,Nk,H", [(100, 50, 37, 32), (97, 64, 64, 32), (3, 1, 5, 7),
                                        (130, 33, 64, 24), (2, 64, 1, 3)])
-def test_short_sequences_every_element(B, Nq, Nk, H):
-    """At most 64 query rows and keys per (batch, head) at D = 64, many (batch, head)
-    pairs: one key tile per two-wave workgroup; ragged row and key counts, one wave idle
-    when Nq <= 32."""
-    D = 64
+def test_short_sequences_every_element(B, Nq, Nk, H, D):
+    """At most 64 query rows and keys per (batch, head), many (batch, head) pairs: one
+    key tile per two-wave workgroup (the one-tile kernel); ragged row and key counts,
+    one wave idle when Nq <= 32."""
     plan = attn.attn_plan(B, Nq, Nk, H, D)
     assert plan["splits"] == 1 and plan["waves"] == 2
     say(f"short B{B} Nq{Nq} Nk{Nk} H{H}: {plan}")
@@ -139,6 +139,24 @@ def test_short_sequences_every_element(B, Nq, Nk, H):
     q, k, v = w.tensors()
     got = host(attn.cross(dev(q), dev(k), dev(v)) if Nq != Nk else attn.dense(dev(q), dev(k), dev(v)))
     assert_accepted(got, oracle.attention(q, k, v), f"short B{B} Nq{Nq} Nk{Nk} H{H}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("Nq,Nk,splits,waves", [(200, 64, 1, 4), (96, 50, 1, 4),
+                                                (70, 256, 4, 2), (130, 250, 4, 4)])
+def test_one_tile_key_ranges(Nq, Nk, splits, waves, D):
+    """Calls whose key ranges are one 64-key tile each: short keys under four-wave
+    workgroups, and keys split into 64-key ranges (partials merged by the combine
+    kernel), the last range ragged."""
+    B, H = 3, 5
+    plan = attn.attn_plan(B, Nq, Nk, H, D, splits, waves)
+    assert plan["waves"] == waves and plan["splits"] == splits
+    assert -(-Nk // 64) <= splits  # one 64-key tile per key range
+    w = synth.small("dense", B, Nq, H, D, 1870 + Nq + Nk, Nk=Nk, sigma_qk=2.0)
+    q, k, v = w.tensors()
+    say(f"one-tile ranges D{D} Nq{Nq} Nk{Nk} splits{splits} waves{waves}")
+    assert_accepted(run_ex(q, k, v, splits=splits, waves=waves), oracle.attention(q, k, v),
+                    f"one-tile D{D} Nq{Nq} Nk{Nk} s{splits} w{waves}")
 
 
 def test_short_prefix_keys_from_both_segments():

@@ -44,11 +44,20 @@ namespace {
 
 using namespace dev;
 
+// Waves per SIMD the kernel is compiled for: two with an LDS ring (registers for two
+// score buffers); a call whose key ranges fit one tile (NSLOT = 1) needs one score
+// buffer and no ring, and is bound by memory latency, so it takes more waves.
+template <int D, int NSLOT>
+constexpr int fwd_waves_per_simd() {
+    return NSLOT > 1 ? 2 : (D == 64 ? 4 : 3);
+}
+
 template <int D, int NW, int BN, int NSLOT>
-__global__ __launch_bounds__(NW* kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(NW* kWave) __attribute__((amdgpu_waves_per_eu(
+    fwd_waves_per_simd<D, NSLOT>(), fwd_waves_per_simd<D, NSLOT>()))) void attn_fwd_kernel(FwdParams p) {
     static_assert(D == 64 || D == 128, "head dim");
     static_assert(BN % 32 == 0 && BN <= 128, "key tile");
-    static_assert(NSLOT == 2 || NSLOT == 3, "LDS ring depth");
+    static_assert(NSLOT >= 1 && NSLOT <= 3, "LDS ring depth (1: one tile per workgroup)");
     constexpr int NB = BN / 32;            // 32-key blocks per tile
     constexpr int KS = D / 16;             // MFMA k-steps over the head dim
     constexpr int DB = D / 32;             // 32-wide head-dim blocks of O^T
@@ -334,6 +343,17 @@ __global__ __launch_bounds__(NW* kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
     const int ntiles = (kend - kbeg + BN - 1) / BN;
     auto kslot = [&](int j) { return smem + (j % NSLOT) * TILEB; };
     auto vslot = [&](int j) { return smem + (NSLOT + j % NSLOT) * TILEB; };
+    if constexpr (NSLOT == 1) {
+        // every key range of the call is one tile (the launcher checks it)
+        issue_k(kbeg, 0);
+        issue_v(kbeg, 0);
+        barrier_vmcnt<0>();
+        if (active) {
+            f32x16 s1[NB];
+            qk_full(kslot(0), s1);
+            tile_last(s1, kbeg, vslot(0));
+        }
+    } else {
     issue_k(kbeg, 0);
     issue_v(kbeg, 0);
     if (ntiles > 1) {
@@ -395,6 +415,7 @@ __global__ __launch_bounds__(NW* kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
     if (active) {
         const int tl = t + rest;
         tile_last((rest % 2 == 0) ? sA : sB, kbeg + tl * BN, vslot(tl));
+    }
     }
 
     if (!active) return;
@@ -478,6 +499,13 @@ static hipError_t launch_fwd_t(const FwdParams& p, long long workgroups, hipStre
     // Key tile and LDS ring depth: 64-key tiles in three slots at D = 64; at D = 128
     // with 4 waves, 64-key tiles in two slots (64 KiB, two workgroups per CU); with 2
     // waves, 32-key tiles in three slots (48 KiB, three workgroups per CU).
+    // When every key range is one 64-key tile (short sequences), one tile in LDS and no
+    // ring, with more workgroups per CU.
+    if (p.keys_per_split <= kKeyTile) {
+        hipLaunchKernelGGL((attn_fwd_kernel<D, NW, kKeyTile, 1>), dim3((unsigned)workgroups),
+                           dim3(NW * kWave), 0, stream, p);
+        return hipGetLastError();
+    }
     constexpr int BN = (D == 128 && NW == 2) ? 32 : kKeyTile;
     constexpr int NSLOT = (D == 128 && NW == 4) ? 2 : 3;
     hipLaunchKernelGGL((attn_fwd_kernel<D, NW, BN, NSLOT>), dim3((unsigned)workgroups),

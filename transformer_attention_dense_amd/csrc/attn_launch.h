@@ -55,6 +55,7 @@ struct NaParams {
     int qb;       // 16, 8 or 4
     int strips;   // ceil(X / qb): strips of qb positions on the X axis
     int yblocks;  // ceil(Y / (4 * 32 / qb)): blocks of rows y of a workgroup
+    int t_inner;  // workgroup order within a head (na_decode): t fastest (1) or slowest (0)
 };
 void na3d_configure(NaParams& p);
 long long na3d_workgroups(const NaParams& p);

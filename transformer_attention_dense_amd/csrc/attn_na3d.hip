@@ -26,6 +26,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "attn_device.h"
 #include "attn_launch.h"
 
@@ -54,6 +56,37 @@ __device__ __forceinline__ void barrier_tiles_left(int left) {
 }
 
 constexpr int kNaWaves = 4;  // waves per workgroup, stacked on Y
+
+// Workgroup -> (b, t, block of YB rows y, strip of QB positions on X, h). Each XCD
+// (it runs the workgroups whose linear ids are equal mod 8) gets a contiguous range of
+// the order (b, h, ...), so the workgroups of a head, whose windows share K/V rows, run
+// on one XCD and meet the rows in its L2. Within a head: t slowest, then the block of
+// rows y, strip fastest; or (t_inner) t fastest, then strip, block of rows slowest,
+// which the host picks when a head has to be shared by several XCDs and cutting it
+// along Y or X duplicates fewer K/V rows than cutting it along T.
+__device__ __forceinline__ void na_decode(const NaParams& p, int& b, int& t, int& yblk,
+                                          int& strip, int& h) {
+    long idx = blockIdx.x;
+    const long per = (long)gridDim.x >> 3;
+    if (idx < (per << 3)) idx = (idx & 7) * per + (idx >> 3);
+    if (p.t_inner) {
+        t = (int)(idx % p.T);
+        idx /= p.T;
+        strip = (int)(idx % p.strips);
+        idx /= p.strips;
+        yblk = (int)(idx % p.yblocks);
+        idx /= p.yblocks;
+    } else {
+        strip = (int)(idx % p.strips);
+        idx /= p.strips;
+        yblk = (int)(idx % p.yblocks);
+        idx /= p.yblocks;
+        t = (int)(idx % p.T);
+        idx /= p.T;
+    }
+    h = (int)(idx % p.H);
+    b = (int)(idx / p.H);
+}
 
 // Query tile of a wave: QA rows y x QB positions on X (32 queries). A key block is RPB
 // rows of KW positions on X (32 keys), the X windows of the QB positions lying in the KW
@@ -96,16 +129,8 @@ void attn_na3d_kernel(NaParams p) {
     const int n = lane & 31;
     const int g = lane >> 5;
 
-    // workgroup -> (b, t, block of YB rows y, strip of QB positions on X, h), h fastest
-    long idx = blockIdx.x;
-    const int h = (int)(idx % p.H);
-    idx /= p.H;
-    const int strip = (int)(idx % p.strips);
-    idx /= p.strips;
-    const int yblk = (int)(idx % p.yblocks);
-    idx /= p.yblocks;
-    const int t = (int)(idx % p.T);
-    const int b = (int)(idx / p.T);
+    int b, t, yblk, strip, h;
+    na_decode(p, b, t, yblk, strip, h);
 
     const int X = p.X, Y = p.Y;
     const long HD = (long)p.H * D;
@@ -324,6 +349,22 @@ void na3d_configure(NaParams& p) {
             p.strips = (p.X + o.qb - 1) / o.qb;
             p.yblocks = (p.Y + kNaWaves * o.qa - 1) / (kNaWaves * o.qa);
         }
+    }
+    // Heads shared by n XCDs are cut along the slowest axis of the order: T (t slowest),
+    // else the blocks of rows y, or the strips when there is one block of rows. Each part
+    // fetches the K/V rows of its range plus the window's halo; take the cheaper cut.
+    p.t_inner = 0;
+    const long heads = (long)p.B * p.H;
+    if (heads < 8 && p.qb) {
+        const int n = (int)((8 + heads - 1) / heads);
+        auto dup = [n](int len, int win) {  // K/V rows read per row of the axis
+            const double part = (double)len / n;
+            return n * std::min((double)len, part + win - 1) / len;
+        };
+        const double cut_t = p.T >= n ? dup(p.T, p.kt) : 1e30;
+        const double cut_yx = p.yblocks >= n ? dup(p.Y, p.ky)
+                              : (p.yblocks == 1 && p.strips >= n ? dup(p.X, p.kx) : 1e30);
+        p.t_inner = cut_yx < cut_t ? 1 : 0;
     }
 }
 
