@@ -46,10 +46,11 @@ using namespace dev;
 
 // Waves per SIMD the kernel is compiled for: two with an LDS ring (registers for two
 // score buffers); a call whose key ranges fit one tile (NSLOT = 1) needs one score
-// buffer and no ring, and is bound by memory latency, so it takes more waves.
+// buffer and no ring: three at D = 64, where the LDS (K, V, and the query rows) still
+// holds six two-wave workgroups per CU.
 template <int D, int NSLOT>
 constexpr int fwd_waves_per_simd() {
-    return NSLOT > 1 ? 2 : (D == 64 ? 4 : 3);
+    return (NSLOT == 1 && D == 64) ? 3 : 2;
 }
 
 template <int D, int NW, int BN, int NSLOT>
@@ -68,8 +69,10 @@ __global__ __launch_bounds__(NW* kWave) __attribute__((amdgpu_waves_per_eu(
     constexpr int PER_T = BN * CPR / NT;   // 16-byte loads per thread per tensor per tile
     static_assert(BN * CPR % NT == 0 && NT % CPR == 0, "loader");
 
-    // Three K slots then three V slots, rows of 2*D bytes, chunks swizzled.
-    __shared__ __attribute__((aligned(1024))) char smem[2 * NSLOT * TILEB];
+    // Three K slots then three V slots, rows of 2*D bytes, chunks swizzled. One-tile
+    // calls add each wave's 32 query rows, which also stage its output rows.
+    constexpr int QOB = (NSLOT == 1) ? NW * 32 * ROWB : 0;
+    __shared__ __attribute__((aligned(1024))) char smem[2 * NSLOT * TILEB + QOB];
 
     int mb, bh, split;
     decode_workgroup(p.m_blocks, p.B * p.H, mb, bh, split);
@@ -99,15 +102,32 @@ __global__ __launch_bounds__(NW* kWave) __attribute__((amdgpu_waves_per_eu(
         uniform_ptr(p.v1 ? p.v1 + ((long)b * p.n1 * HD + (long)h * D) : vseg0);
 
     // Q^T fragments (B operand), one per 16-dim k-step: lane holds query n, dims
-    // 16*ks + 8g .. +7.
+    // 16*ks + 8g .. +7. One-tile calls read them from LDS after the copies below.
     bf16x8 qf[KS];
-    {
+    if constexpr (NSLOT != 1) {
         const int qi = min(q0 + n, p.Nq - 1);
         const uint16_t* qrow = p.q + ((long)(b * p.Nq + qi) * H + h) * D;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
             qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks + 8 * g);
     }
+    // One-tile calls: the wave's rows of Q go global -> LDS as whole rows (lane i of
+    // round r copies 16-byte chunk 64 r + i of the wave's 32 rows, swizzled like the
+    // K/V rows), and the output leaves through the same rows: a wave's loads and stores
+    // then cover whole 128- or 256-byte rows instead of 16- to 32-byte pieces of 32
+    // rows, which matters when every workgroup moves only a few KiB.
+    char* const qo = smem + 2 * NSLOT * TILEB + wave * 32 * ROWB;
+    auto issue_q = [&]() {
+        static_for<CPR / 2>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            const int id = i * kWave + lane;
+            const int r = id / CPR;
+            const int lc = (id % CPR) ^ lds_swizzle<CPR>(r);
+            const int qi = min(q0 + r, p.Nq - 1);
+            load16_to_lds(p.q + ((long)(b * p.Nq + qi) * H + h) * D + lc * 8,
+                          qo + i * kWave * 16);
+        });
+    };
 
     // Loader: load round i of thread tid fills physical chunk P = i*NT + tid of a
     // tile, i.e. row r = P / CPR at chunk position P % CPR, which holds logical chunk
@@ -345,10 +365,15 @@ __global__ __launch_bounds__(NW* kWave) __attribute__((amdgpu_waves_per_eu(
     auto vslot = [&](int j) { return smem + (NSLOT + j % NSLOT) * TILEB; };
     if constexpr (NSLOT == 1) {
         // every key range of the call is one tile (the launcher checks it)
+        issue_q();
         issue_k(kbeg, 0);
         issue_v(kbeg, 0);
         barrier_vmcnt<0>();
         if (active) {
+            const int tsw = lds_swizzle<CPR>(n) ^ g;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                qf[ks] = *reinterpret_cast<const bf16x8*>(qo + n * ROWB + 16 * ((2 * ks) ^ tsw));
             f32x16 s1[NB];
             qk_full(kslot(0), s1);
             tile_last(s1, kbeg, vslot(0));
@@ -423,7 +448,34 @@ __global__ __launch_bounds__(NW* kWave) __attribute__((amdgpu_waves_per_eu(
     // ---- epilogue
     const float l_tot = wave_swap_sum(l_part);
     const int qi = q0 + n;
-    if (p.splits == 1) {
+    if (NSLOT == 1 && p.splits == 1) {
+        // through the wave's LDS rows: row n, chunk 4 db + j holds dims 32 db + 8 j ..
+        const float inv = 1.0f / l_tot;
+        const int sw = lds_swizzle<CPR>(n);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                bf16x4 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = (__bf16)(o[db][4 * j + e] * inv);
+                *reinterpret_cast<bf16x4*>(qo + n * ROWB + 16 * ((4 * db + j) ^ sw) + 8 * g) = v;
+            }
+        __asm__ volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
+        __asm__ volatile("" ::: "memory");
+        static_for<CPR / 2>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            const int id = i * kWave + lane;
+            const int r = id / CPR;
+            const int pc = id % CPR;
+            const int lc = pc ^ lds_swizzle<CPR>(r);
+            const uint4 v = *reinterpret_cast<const uint4*>(qo + r * ROWB + 16 * pc);
+            if (q0 + r < p.Nq)
+                *reinterpret_cast<uint4*>(p.out + ((long)(b * p.Nq + q0 + r) * H + h) * D +
+                                          lc * 8) = v;
+        });
+    } else if (p.splits == 1) {
         const float inv = 1.0f / l_tot;
         if (qi < p.Nq) {
             uint16_t* orow = p.out + ((long)(b * p.Nq + qi) * H + h) * D;

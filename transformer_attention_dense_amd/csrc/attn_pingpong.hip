@@ -540,19 +540,39 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const float l_tot = wave_swap_sum(l_part);
     const int qi = q0 + n;
     if (p.splits == 1) {
+        // The output rows go out through LDS so that each store covers whole rows (16
+        // or 8 lanes per row) rather than 8 bytes of 32 rows. After the last barrier no
+        // wave reads the K slots or the two V slots other than the last tile's: group 0
+        // stages in the K slots, group 1 (still reading the last V tile) in those two.
+        constexpr int WB = 32 * ROWB;  // one wave's rows
+        static_assert(NSLOT * TILEB >= 4 * WB && TILEB == 2 * WB, "staging space");
+        char* const stage = (grp == 0) ? smem + wave * WB
+                                       : vslot((T + (wave - 4) / 2) % NSLOT) + ((wave - 4) % 2) * WB;
         const float inv = 1.0f / l_tot;
-        if (qi < p.Nq) {
-            uint16_t* orow = p.out + ((long)(b * p.Nq + qi) * H + h) * D;
+        const int sw = lds_swizzle<CPR>(n);
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    bf16x4 v;
+            for (int j = 0; j < 4; ++j) {
+                bf16x4 v;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = (__bf16)(o[db][4 * j + e] * inv);
-                    *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * j + 4 * g) = v;
-                }
-        }
+                for (int e = 0; e < 4; ++e) v[e] = (__bf16)(o[db][4 * j + e] * inv);
+                // row n, chunk 4 db + j holds dims 32 db + 8 j ..
+                *reinterpret_cast<bf16x4*>(stage + n * ROWB + 16 * ((4 * db + j) ^ sw) + 8 * g) = v;
+            }
+        __asm__ volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
+        __asm__ volatile("" ::: "memory");
+        static_for<CPR / 2>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            const int id = i * kWave + lane;
+            const int r = id / CPR;
+            const int pc = id % CPR;
+            const uint4 v = *reinterpret_cast<const uint4*>(stage + r * ROWB + 16 * pc);
+            if (q0 + r < p.Nq)
+                *reinterpret_cast<uint4*>(p.out + ((long)(b * p.Nq + q0 + r) * H + h) * D +
+                                          (pc ^ lds_swizzle<CPR>(r)) * 8) = v;
+        });
     } else {
         const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
         if (qi < p.Nq) {
