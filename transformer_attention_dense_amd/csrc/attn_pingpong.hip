@@ -88,7 +88,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     static_assert(BN * CPR % NT == 0 && RSTEP % 16 == 0, "loader pattern");
     static_assert(BN * CPR % NTG == 0 && RSTEP_G % 16 == 0, "group loader pattern");
 
-    __shared__ __attribute__((aligned(1024))) char smem[2 * NSLOT * TILEB];
+    // K ring, V ring, then each wave's 32 query rows (Q on the way in, O on the way out)
+    constexpr int WB = 32 * ROWB;
+    __shared__ __attribute__((aligned(1024))) char smem[2 * NSLOT * TILEB + NW * WB];
 
     int mb, bh, split;
     decode_workgroup(p.m_blocks, p.B * p.H, mb, bh, split, BC);
@@ -137,14 +139,22 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         uniform_ptr(p.v1 ? p.v1 + ((long)b * p.n1 * HD + (long)h * D) : vseg0);
 
     // Q^T fragments (B operand): lane holds query n, dims 16*ks + 8g .. +7.
+    // They arrive through the wave's LDS rows (below): lane i of round r copies 16-byte
+    // chunk 64 r + i of the wave's 32 rows, swizzled like the K/V rows, so each copy
+    // instruction covers whole rows rather than 32 bytes of 32 rows.
     bf16x8 qf[KS];
-    {
-        const int qi = min(q0 + n, p.Nq - 1);
-        const uint16_t* qrow = p.q + ((long)(b * p.Nq + qi) * H + h) * D;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks + 8 * g);
-    }
+    char* const qo = smem + 2 * NSLOT * TILEB + wave * WB;
+    auto issue_q = [&]() {
+        static_for<CPR / 2>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            const int id = i * kWave + lane;
+            const int r = id / CPR;
+            const int lc = (id % CPR) ^ lds_swizzle<CPR>(r);
+            const int qi = min(q0 + r, p.Nq - 1);
+            load16_to_lds(p.q + ((long)(b * p.Nq + qi) * H + h) * D + lc * 8,
+                          qo + i * kWave * 16);
+        });
+    };
 
     // Loader: copy round i of thread tid fills physical chunk i*NT + tid of a tile:
     // row r = (i*NT + tid) / CPR, chunk position tid % CPR holding logical chunk
@@ -448,11 +458,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
 
-    // ---- prologue: K(0), K(1), V(0) resident before phase 0
+    // ---- prologue: the wave's Q rows, K(0), K(1), V(0) resident before phase 0
+    issue_q();
     issue_k(kbeg, 0);
     if (T > 1) issue_k(kbeg + BN, 1);
     issue_v(kbeg, 0);
     barrier_vmcnt<0>();
+    {
+        const int tsw = lds_swizzle<CPR>(n) ^ g;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            qf[ks] = *reinterpret_cast<const bf16x8*>(qo + n * ROWB + 16 * ((2 * ks) ^ tsw));
+    }
 
     // Each group runs its own straight-line phase sequence; both execute the same
     // barriers in the same order. Group 0: G(u) then S(u) in tile u; group 1: S(u-1)
@@ -540,14 +557,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const float l_tot = wave_swap_sum(l_part);
     const int qi = q0 + n;
     if (p.splits == 1) {
-        // The output rows go out through LDS so that each store covers whole rows (16
-        // or 8 lanes per row) rather than 8 bytes of 32 rows. After the last barrier no
-        // wave reads the K slots or the two V slots other than the last tile's: group 0
-        // stages in the K slots, group 1 (still reading the last V tile) in those two.
-        constexpr int WB = 32 * ROWB;  // one wave's rows
-        static_assert(NSLOT * TILEB >= 4 * WB && TILEB == 2 * WB, "staging space");
-        char* const stage = (grp == 0) ? smem + wave * WB
-                                       : vslot((T + (wave - 4) / 2) % NSLOT) + ((wave - 4) % 2) * WB;
+        // The output rows go out through the wave's LDS rows so that each store covers
+        // whole rows (16 or 8 lanes per row) rather than 8 bytes of 32 rows.
+        char* const stage = qo;
         const float inv = 1.0f / l_tot;
         const int sw = lds_swizzle<CPR>(n);
 #pragma unroll
