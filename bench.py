@@ -390,16 +390,19 @@ def bench_one(w, steps, warmup, warmup_seconds, torch, attn, ts):
             "inputs_unchanged": inputs_unchanged}
 
 
-def kernel_name(D, plan):
+def kernel_name(D, plan, keys):
     """The kernel(s) a launch of this plan runs (as rocprofv3 names them)."""
     waves = plan["waves"]
     if plan.get("block_causal"):
         return f"attn_bc_meta_kernel + attn_fwd_pp_kernel<{D}, true>"
     if plan.get("na3d"):
         return f"attn_na3d_kernel<{plan['query_tile'][1]}>"
-    # attn_fwd_kernel<D, waves, keys per tile, LDS slots>, as the library instantiates it
+    # attn_fwd_kernel<D, waves, keys per tile, LDS slots>, as the library instantiates it:
+    # one slot when every key range is one 64-key tile
     bn = 32 if (D == 128 and waves == 2) else 64
     nslot = 2 if (D == 128 and waves == 4) else 3
+    if -(-keys // 64) <= plan["splits"]:
+        bn, nslot = 64, 1
     main = (f"attn_fwd_pp_kernel<{D}, false>" if waves == 8 else
             f"attn_fwd_kernel<{D}, {waves}, {bn}, {nslot}>")
     return main if plan["splits"] == 1 else main + f" + attn_combine_kernel<{D}>"
@@ -442,7 +445,7 @@ def record(w, r, steps, warmup, cpu, check, env):
             "traffic": hbm,
             "traffic_source": (f"profiles/traffic.json (counter runs on kernel sources "
                                f"{stored.get('kernel_source_hash')})" if hbm else None),
-            "kernel": kernel_name(w.D, r["plan"]),
+            "kernel": kernel_name(w.D, r["plan"], w.keys),
             "avg_launch_us": round(launch_us, 2),
             "algorithmic_flop_per_launch": w.flop,
             "algorithmic_bytes_per_launch": w.algorithmic_bytes,

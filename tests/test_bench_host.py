@@ -102,3 +102,13 @@ def test_output_check_covers_only_the_rows_the_oracle_computed():
     out[5:] = 0x4000  # 2.0 in BF16, beyond the checked rows
     res = bench.check_output(out, ref, 64)
     assert res["ok"] and res["rows_checked"] == 3 and res["rows_total"] == 10
+
+
+def test_kernel_names_follow_the_library_instantiation():
+    """The bench names the kernel a plan runs as rocprofv3 reports it."""
+    assert bench.kernel_name(128, {"waves": 8, "splits": 1}, 4096) == "attn_fwd_pp_kernel<128, false>"
+    assert bench.kernel_name(64, {"waves": 2, "splits": 1}, 64) == "attn_fwd_kernel<64, 2, 64, 1>"
+    assert bench.kernel_name(64, {"waves": 2, "splits": 1}, 256) == "attn_fwd_kernel<64, 2, 64, 3>"
+    assert bench.kernel_name(128, {"waves": 2, "splits": 1}, 100) == "attn_fwd_kernel<128, 2, 32, 3>"
+    assert (bench.kernel_name(128, {"waves": 4, "splits": 4}, 256)
+            == "attn_fwd_kernel<128, 4, 64, 1> + attn_combine_kernel<128>")
