@@ -186,5 +186,74 @@ __device__ __forceinline__ void barrier_vmcnt() {
     __asm__ volatile("" ::: "memory");
 }
 
+// One wave's 32 rows of D BF16 values through LDS, as whole rows. Row r of the wave
+// is at base + r * stride (elements); rows at or past nvalid are clamped to the last
+// valid one on the way in and skipped on the way out. In LDS the rows are 2*D bytes
+// with 16-byte chunks swizzled like the K/V tiles, so a lane's 16-byte chunk of a row
+// is read and written without bank conflicts. Lane i of round k moves chunk 64 k + i.
+//
+// Copy in: global -> LDS (global_load_lds_dwordx4, D/16 copies per lane); the caller
+// waits for them (vmcnt) before reading the rows.
+template <int D>
+__device__ __forceinline__ void copy_wave_rows_to_lds(const uint16_t* base, long stride,
+                                                      int nvalid, char* rows) {
+    constexpr int CPR = D / 8;
+    const int lane = threadIdx.x % kWave;
+    static_for<CPR / 2>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        const int id = i * kWave + lane;
+        const int r = id / CPR;
+        const int lc = (id % CPR) ^ lds_swizzle<CPR>(r);
+        load16_to_lds(base + (long)min(r, nvalid - 1) * stride + lc * 8, rows + i * kWave * 16);
+    });
+}
+
+// The Q^T fragments of the rows: lane (n, g) holds row n, elements 16 ks + 8 g .. +7.
+template <int D>
+__device__ __forceinline__ void read_wave_rows_qf(const char* rows, bf16x8 (&qf)[D / 16]) {
+    constexpr int CPR = D / 8;
+    const int lane = threadIdx.x % kWave;
+    const int n = lane & 31, g = lane >> 5;
+    const int tsw = lds_swizzle<CPR>(n) ^ g;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+        qf[ks] = *reinterpret_cast<const bf16x8*>(rows + n * 2 * D + 16 * ((2 * ks) ^ tsw));
+}
+
+// Store out: the wave's O^T accumulators (o[db][4 j + e] holds row n, element
+// 32 db + 8 j + 4 g + e, for lane (n, g)) times inv, rounded to BF16, go to its LDS rows
+// and from there to global memory, each store instruction covering whole rows.
+template <int D>
+__device__ __forceinline__ void store_wave_rows_via_lds(const f32x16 (&o)[D / 32], float inv,
+                                                        char* rows, uint16_t* base,
+                                                        long stride, int nvalid) {
+    constexpr int CPR = D / 8;
+    const int lane = threadIdx.x % kWave;
+    const int n = lane & 31, g = lane >> 5;
+    const int sw = lds_swizzle<CPR>(n);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            bf16x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = (__bf16)(o[db][4 * j + e] * inv);
+            *reinterpret_cast<bf16x4*>(rows + n * 2 * D + 16 * ((4 * db + j) ^ sw) + 8 * g) = v;
+        }
+    // the rows are read back by other lanes of the wave: LDS writes complete first
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
+    __asm__ volatile("" ::: "memory");
+    static_for<CPR / 2>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        const int id = i * kWave + lane;
+        const int r = id / CPR;
+        const int pc = id % CPR;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(rows + r * 2 * D + 16 * pc);
+        if (r < nvalid)
+            *reinterpret_cast<u32x4*>(base + (long)r * stride + (pc ^ lds_swizzle<CPR>(r)) * 8) = v;
+    });
+}
+
 }  // namespace dev
 }  // namespace attn

@@ -111,23 +111,12 @@ __global__ __launch_bounds__(NW* kWave) __attribute__((amdgpu_waves_per_eu(
         for (int ks = 0; ks < KS; ++ks)
             qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks + 8 * g);
     }
-    // One-tile calls: the wave's rows of Q go global -> LDS as whole rows (lane i of
-    // round r copies 16-byte chunk 64 r + i of the wave's 32 rows, swizzled like the
-    // K/V rows), and the output leaves through the same rows: a wave's loads and stores
-    // then cover whole 128- or 256-byte rows instead of 16- to 32-byte pieces of 32
-    // rows, which matters when every workgroup moves only a few KiB.
+    // One-tile calls: the wave's rows of Q arrive through LDS as whole rows and the
+    // output leaves through the same rows, so a wave's loads and stores cover whole
+    // 128- or 256-byte rows instead of 16- to 32-byte pieces of 32 rows, which matters
+    // when every workgroup moves only a few KiB.
     char* const qo = smem + 2 * NSLOT * TILEB + wave * 32 * ROWB;
-    auto issue_q = [&]() {
-        static_for<CPR / 2>([&](auto ic) {
-            constexpr int i = decltype(ic)::value;
-            const int id = i * kWave + lane;
-            const int r = id / CPR;
-            const int lc = (id % CPR) ^ lds_swizzle<CPR>(r);
-            const int qi = min(q0 + r, p.Nq - 1);
-            load16_to_lds(p.q + ((long)(b * p.Nq + qi) * H + h) * D + lc * 8,
-                          qo + i * kWave * 16);
-        });
-    };
+    const long qrow0 = ((long)b * p.Nq * H + (long)q0 * H + h) * D;  // the wave's row 0
 
     // Loader: load round i of thread tid fills physical chunk P = i*NT + tid of a
     // tile, i.e. row r = P / CPR at chunk position P % CPR, which holds logical chunk
@@ -365,15 +354,12 @@ __global__ __launch_bounds__(NW* kWave) __attribute__((amdgpu_waves_per_eu(
     auto vslot = [&](int j) { return smem + (NSLOT + j % NSLOT) * TILEB; };
     if constexpr (NSLOT == 1) {
         // every key range of the call is one tile (the launcher checks it)
-        issue_q();
+        copy_wave_rows_to_lds<D>(p.q + qrow0, HD, p.Nq - q0, qo);
         issue_k(kbeg, 0);
         issue_v(kbeg, 0);
         barrier_vmcnt<0>();
         if (active) {
-            const int tsw = lds_swizzle<CPR>(n) ^ g;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                qf[ks] = *reinterpret_cast<const bf16x8*>(qo + n * ROWB + 16 * ((2 * ks) ^ tsw));
+            read_wave_rows_qf<D>(qo, qf);
             f32x16 s1[NB];
             qk_full(kslot(0), s1);
             tile_last(s1, kbeg, vslot(0));
@@ -449,32 +435,7 @@ __global__ __launch_bounds__(NW* kWave) __attribute__((amdgpu_waves_per_eu(
     const float l_tot = wave_swap_sum(l_part);
     const int qi = q0 + n;
     if (NSLOT == 1 && p.splits == 1) {
-        // through the wave's LDS rows: row n, chunk 4 db + j holds dims 32 db + 8 j ..
-        const float inv = 1.0f / l_tot;
-        const int sw = lds_swizzle<CPR>(n);
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                bf16x4 v;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = (__bf16)(o[db][4 * j + e] * inv);
-                *reinterpret_cast<bf16x4*>(qo + n * ROWB + 16 * ((4 * db + j) ^ sw) + 8 * g) = v;
-            }
-        __asm__ volatile("" ::: "memory");
-        __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
-        __asm__ volatile("" ::: "memory");
-        static_for<CPR / 2>([&](auto ic) {
-            constexpr int i = decltype(ic)::value;
-            const int id = i * kWave + lane;
-            const int r = id / CPR;
-            const int pc = id % CPR;
-            const int lc = pc ^ lds_swizzle<CPR>(r);
-            const uint4 v = *reinterpret_cast<const uint4*>(qo + r * ROWB + 16 * pc);
-            if (q0 + r < p.Nq)
-                *reinterpret_cast<uint4*>(p.out + ((long)(b * p.Nq + q0 + r) * H + h) * D +
-                                          lc * 8) = v;
-        });
+        store_wave_rows_via_lds<D>(o, 1.0f / l_tot, qo, p.out + qrow0, HD, p.Nq - q0);
     } else if (p.splits == 1) {
         const float inv = 1.0f / l_tot;
         if (qi < p.Nq) {
