@@ -222,7 +222,41 @@ __device__ __forceinline__ void read_wave_rows_qf(const char* rows, bf16x8 (&qf)
 
 // Store out: the wave's O^T accumulators (o[db][4 j + e] holds row n, element
 // 32 db + 8 j + 4 g + e, for lane (n, g)) times inv, rounded to BF16, go to its LDS rows
-// and from there to global memory, each store instruction covering whole rows.
+// and from there to global memory, each store instruction covering whole rows. Row r
+// goes to row_ptr(r), or nowhere when that is null.
+template <int D, typename RowPtr>
+__device__ __forceinline__ void store_wave_rows_via_lds_to(const f32x16 (&o)[D / 32],
+                                                           float inv, char* rows,
+                                                           RowPtr row_ptr) {
+    constexpr int CPR = D / 8;
+    const int lane = threadIdx.x % kWave;
+    const int n = lane & 31, g = lane >> 5;
+    const int sw = lds_swizzle<CPR>(n);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            bf16x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = (__bf16)(o[db][4 * j + e] * inv);
+            *reinterpret_cast<bf16x4*>(rows + n * 2 * D + 16 * ((4 * db + j) ^ sw) + 8 * g) = v;
+        }
+    // the rows are read back by other lanes of the wave: LDS writes complete first
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
+    __asm__ volatile("" ::: "memory");
+    static_for<CPR / 2>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        const int id = i * kWave + lane;
+        const int r = id / CPR;
+        const int pc = id % CPR;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(rows + r * 2 * D + 16 * pc);
+        uint16_t* dst = row_ptr(r);
+        if (dst) *reinterpret_cast<u32x4*>(dst + (pc ^ lds_swizzle<CPR>(r)) * 8) = v;
+    });
+}
+
+// The same for rows `stride` elements apart from base, of which the first nvalid exist.
 template <int D>
 __device__ __forceinline__ void store_wave_rows_via_lds(const f32x16 (&o)[D / 32], float inv,
                                                         char* rows, uint16_t* base,

@@ -138,7 +138,6 @@ void attn_na3d_kernel(NaParams p) {
     const bool active = wy0 < Y;
     const int yq = wy0 + n / QB;            // this lane's query row
     const int xq = strip * QB + n % QB;     // and position on X
-    const bool qvalid = yq < Y && xq < X;
     const int yqc = min(yq, Y - 1), xqc = min(xq, X - 1);
     const long pos_q = (((long)b * p.T + t) * Y + yqc) * X + xqc;
 
@@ -314,18 +313,16 @@ void attn_na3d_kernel(NaParams p) {
     // ---- epilogue
     if (!active) return;
     const float l_tot = wave_swap_sum(l_part);
-    if (!qvalid) return;
-    const float inv = 1.0f / l_tot;
-    uint16_t* orow = p.out + pos_q * HD + (long)h * D;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            bf16x4 v;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = (__bf16)(o[db][4 * j + e] * inv);
-            *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * j + 4 * g) = v;
-        }
+    // Through LDS, whole 128-byte rows per store: after the last block's barrier only
+    // that block's slot is read, so two of the other slots (8 KiB each) hold the four
+    // waves' rows. Row r of the wave is query (wy0 + r / QB, strip * QB + r % QB).
+    char* const rows = smem + ((nblocks + wave / 2) % NSLOT) * 2 * TILEB + (wave % 2) * (32 * ROWB);
+    const long frame = ((long)b * p.T + t) * Y;
+    store_wave_rows_via_lds_to<D>(o, 1.0f / l_tot, rows, [&](int r) -> uint16_t* {
+        const int yr = wy0 + r / QB, xr = strip * QB + r % QB;
+        if (yr >= Y || xr >= X) return nullptr;
+        return p.out + ((frame + yr) * X + xr) * HD + (long)h * D;
+    });
 }
 
 }  // namespace
