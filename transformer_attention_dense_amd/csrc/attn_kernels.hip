@@ -434,22 +434,13 @@ __global__ __launch_bounds__(NW* kWave) __attribute__((amdgpu_waves_per_eu(
     // ---- epilogue
     const float l_tot = wave_swap_sum(l_part);
     const int qi = q0 + n;
-    if (NSLOT == 1 && p.splits == 1) {
-        store_wave_rows_via_lds<D>(o, 1.0f / l_tot, qo, p.out + qrow0, HD, p.Nq - q0);
-    } else if (p.splits == 1) {
-        const float inv = 1.0f / l_tot;
-        if (qi < p.Nq) {
-            uint16_t* orow = p.out + ((long)(b * p.Nq + qi) * H + h) * D;
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    bf16x4 v;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = (__bf16)(o[db][4 * j + e] * inv);
-                    *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * j + 4 * g) = v;
-                }
-        }
+    if (p.splits == 1) {
+        // Whole-row stores through LDS: the one-tile form has its own rows; with a ring,
+        // no wave reads a K slot after the last tile barrier, and the K slots hold every
+        // wave's 32 rows.
+        static_assert(NSLOT == 1 || NSLOT * TILEB >= NW * 32 * ROWB, "staging space");
+        char* const rows = (NSLOT == 1) ? qo : smem + wave * 32 * ROWB;
+        store_wave_rows_via_lds<D>(o, 1.0f / l_tot, rows, p.out + qrow0, HD, p.Nq - q0);
     } else {
         const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
         if (qi < p.Nq) {
