@@ -289,5 +289,49 @@ __device__ __forceinline__ void store_wave_rows_via_lds(const f32x16 (&o)[D / 32
     });
 }
 
+// FP32 rows (split-KV partial outputs, D floats per row) through the same 32 × 2·D-byte
+// LDS rows, in two passes of D/2 floats: in pass p lane (n, g) writes, for each of its
+// head-dim blocks db of that half and each j, the four floats of elements
+// 32 db + 8 j + 4 g .. as one 16-byte chunk; then whole half-rows go out.
+template <int D>
+__device__ __forceinline__ void store_wave_rows_f32_via_lds(const f32x16 (&o)[D / 32],
+                                                            float inv, char* rows, float* base,
+                                                            long stride, int nvalid) {
+    constexpr int CPR = D / 8;  // 16-byte chunks in half a row of D floats
+    constexpr int DBH = D / 64;  // head-dim blocks per half
+    const int lane = threadIdx.x % kWave;
+    const int n = lane & 31, g = lane >> 5;
+    const int sw = lds_swizzle<CPR>(n);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+        for (int d = 0; d < DBH; ++d)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                f32x4 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = o[half * DBH + d][4 * j + e] * inv;
+                *reinterpret_cast<f32x4*>(rows + n * 2 * D + 16 * ((8 * d + 2 * j + g) ^ sw)) = v;
+            }
+        __asm__ volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
+        __asm__ volatile("" ::: "memory");
+        static_for<CPR / 2>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            const int id = i * kWave + lane;
+            const int r = id / CPR;
+            const int pc = id % CPR;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(rows + r * 2 * D + 16 * pc);
+            if (r < nvalid)
+                *reinterpret_cast<u32x4*>(base + (long)r * stride + half * (D / 2) +
+                                          (pc ^ lds_swizzle<CPR>(r)) * 4) = v;
+        });
+        // the next pass rewrites the rows: these reads complete first
+        __asm__ volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
+        __asm__ volatile("" ::: "memory");
+    }
+}
+
 }  // namespace dev
 }  // namespace attn

@@ -434,28 +434,21 @@ __global__ __launch_bounds__(NW* kWave) __attribute__((amdgpu_waves_per_eu(
     // ---- epilogue
     const float l_tot = wave_swap_sum(l_part);
     const int qi = q0 + n;
+    // Whole-row stores through LDS: the one-tile form has its own rows; with a ring, no
+    // wave reads a K slot after the last tile barrier, and the K slots hold every wave's
+    // 32 rows of 2·D bytes (BF16 outputs, or FP32 partials half a row at a time).
+    static_assert(NSLOT == 1 || NSLOT * TILEB >= NW * 32 * ROWB, "staging space");
+    char* const stage = (NSLOT == 1) ? qo : smem + wave * 32 * ROWB;
     if (p.splits == 1) {
-        // Whole-row stores through LDS: the one-tile form has its own rows; with a ring,
-        // no wave reads a K slot after the last tile barrier, and the K slots hold every
-        // wave's 32 rows.
-        static_assert(NSLOT == 1 || NSLOT * TILEB >= NW * 32 * ROWB, "staging space");
-        char* const rows = (NSLOT == 1) ? qo : smem + wave * 32 * ROWB;
-        store_wave_rows_via_lds<D>(o, 1.0f / l_tot, rows, p.out + qrow0, HD, p.Nq - q0);
+        store_wave_rows_via_lds<D>(o, 1.0f / l_tot, stage, p.out + qrow0, HD, p.Nq - q0);
     } else {
         const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+        const long rows = (long)p.B * p.Nq * H;
+        store_wave_rows_f32_via_lds<D>(
+            o, inv, stage, p.part_o + ((long)split * rows + (long)(b * p.Nq + q0) * H + h) * D,
+            HD, p.Nq - q0);
         if (qi < p.Nq) {
             const long row = (long)(b * p.Nq + qi) * H + h;
-            const long rows = (long)p.B * p.Nq * H;
-            float* prow = p.part_o + ((long)split * rows + row) * D;
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    f32x4 v;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = o[db][4 * j + e] * inv;
-                    *reinterpret_cast<f32x4*>(prow + 32 * db + 8 * j + 4 * g) = v;
-                }
             if (g == 0) {
                 const float mref2 = (m_ref == -INFINITY) ? 0.f : m_ref * c;
                 p.part_lse[(long)split * rows + row] =
