@@ -156,6 +156,14 @@ def test_set_workspace_checks_before_any_device_work():
     if rc == 0:
         assert attn.attn_set_workspace(None, 0) == 0
     assert attn.attn_plan(1024, 64, 64, 32, 64)["waves"] == 2
+    # the 2- and 4-wave kernels split only while the shorter key loops outweigh the merge:
+    # 256 four-wave workgroups of 16 key tiles stay whole; 32 two-wave ones with 64 key
+    # tiles become 256 (one per CU), 128 with 64 tiles 512 (16 tiles per split)
+    assert attn.attn_plan(1, 1024, 1024, 32, 128) == {"splits": 1, "waves": 4, "workgroups": 256,
+                                                      "workspace_bytes": 0}
+    assert attn.attn_plan(1, 64, 4096, 32, 128)["splits"] == 8
+    assert attn.attn_plan(1, 256, 4096, 32, 128)["splits"] == 4
+    assert attn.attn_plan(1, 256, 1024, 32, 128)["splits"] == 2
     # few query blocks and long keys -> the keys are split and a work space is needed
     ps = attn.attn_plan(1, 64, 8192, 2, 128)
     assert ps["splits"] > 1 and ps["workspace_bytes"] > 0

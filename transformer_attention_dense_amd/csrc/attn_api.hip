@@ -90,12 +90,20 @@ int make_plan(int B, int Nq, int Nk, int H, int D, int num_splits, int waves, Pl
 
     int s = num_splits;
     if (s == 0) {
-        // Split the keys only when the grid underfills the GPU and every split keeps
-        // at least four key tiles. The GPU holds one 8-wave workgroup per CU (96 KiB of
-        // LDS, two waves per SIMD) and two of the 2- and 4-wave ones: 256 CUs x that.
-        const long long target = (w == 8) ? 256 : 512;
+        // Split the keys only when the grid underfills the GPU, keeping at least four key
+        // tiles per split: first up to one workgroup per CU (256 CUs); then, for the 2-
+        // and 4-wave kernels, which hold two or three workgroups per CU, up to two per CU
+        // while every split keeps 16 (2 waves) or 32 (4 waves) tiles, where the shorter
+        // key loops outweigh the merge of the partial results. Measured on MI355X: B=1
+        // N=1024 H=32 D=128 (4 waves) 21.8 us unsplit against 35.1 us in two splits;
+        // Nq=64 Nk=4096 H=32 D=128 (2 waves) best with 8 splits (23.0 us; 27.4 with 16);
+        // Nq=256 Nk=4096 H=32 D=128 best with 4 (39.2 us; 50.3 with 2).
         s = 1;
-        while (base * s * 2 <= target && key_tiles / (s * 2) >= 4) s *= 2;
+        while (base * s * 2 <= 256 && key_tiles / (s * 2) >= 4) s *= 2;
+        if (w != 8) {
+            const int keep = (w == 4) ? 32 : 16;
+            while (base * s * 2 <= 512 && key_tiles / (s * 2) >= keep) s *= 2;
+        }
     }
     if (s > key_tiles) s = key_tiles;
     if (s < 1) s = 1;
