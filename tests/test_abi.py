@@ -162,8 +162,12 @@ def test_set_workspace_checks_before_any_device_work():
     assert attn.attn_plan(1, 1024, 1024, 32, 128) == {"splits": 1, "waves": 4, "workgroups": 256,
                                                       "workspace_bytes": 0}
     assert attn.attn_plan(1, 64, 4096, 32, 128)["splits"] == 8
-    assert attn.attn_plan(1, 256, 4096, 32, 128)["splits"] == 4
     assert attn.attn_plan(1, 256, 1024, 32, 128)["splits"] == 2
+    # small grids take 4 waves (with their splits) over 32 key tiles or more, else 2
+    p = attn.attn_plan(1, 256, 4096, 32, 128)
+    assert p["waves"] == 4 and p["splits"] == 4 and p["workgroups"] == 256
+    assert attn.attn_plan(1, 512, 512, 32, 128)["waves"] == 2
+    assert attn.attn_plan(1, 64, 16384, 32, 64)["waves"] == 2
     # few query blocks and long keys -> the keys are split and a work space is needed
     ps = attn.attn_plan(1, 64, 8192, 2, 128)
     assert ps["splits"] > 1 and ps["workspace_bytes"] > 0

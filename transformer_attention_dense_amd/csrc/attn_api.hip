@@ -74,15 +74,18 @@ int make_plan(int B, int Nq, int Nk, int H, int D, int num_splits, int waves, Pl
         // The 8-wave ping-pong kernel (256 query rows per workgroup, one workgroup per
         // CU) when it alone fills the 256 CUs: at D = 128, and at D = 64 too (2-5% faster
         // than two 4-wave workgroups per CU on B=1..2, N=2048..16384, H=16..32; equal on
-        // B=4 N=1024). Otherwise 4 waves; 2 waves for short query ranges and for grids of
-        // fewer than 256 4-wave workgroups (twice as many workgroups: B=1 N=256 H=32
-        // D=64 measured 6.8 us against 7.4), with the keys split below when needed.
+        // B=4 N=1024). Otherwise 4 waves; 2 waves for query ranges of at most 64 rows, and
+        // for grids of fewer than 256 4-wave workgroups over fewer than 32 key tiles
+        // (twice as many workgroups: B=1 N=256 H=32 D=64 measured 6.8 us against 7.4;
+        // Nq=512 Nk=512 H=32 D=128 14.6 against 22.4). Over longer keys 4 waves with
+        // their splits win: Nq=256 Nk=4096 H=32 D=128 30.5 us against 39.1, Nq=1024
+        // Nk=4096 H=16 48.1 against 64.0.
         const long long pp_blocks = (long long)((Nq + 255) / 256) * B * H;
         const long long blocks4 = (long long)((Nq + 127) / 128) * B * H;
         if (Nq >= 256 && pp_blocks >= 256)
             w = 8;
         else
-            w = (Nq <= 64 || blocks4 < 256) ? 2 : 4;
+            w = (Nq <= 64 || (blocks4 < 256 && key_tiles < 32)) ? 2 : 4;
     }
     const int bm = 32 * w;
     const long long m_blocks = (Nq + bm - 1) / bm;
