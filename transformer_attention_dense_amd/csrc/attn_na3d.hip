@@ -6,12 +6,13 @@
 // inside the axis at its ends).
 //
 // A wave owns 32 queries of one (b, t, h): QA rows y x QB positions on X (QB = 16, 8 or
-// 4, QA = 32 / QB, picked per window shape); a workgroup stacks four waves on Y. Every
+// 4, QA = 32 / QB, picked per window shape); a workgroup stacks four waves on Y, or on T
+// (four frames of the same rows) where their windows overlap more that way. Every
 // (t', y') row of a query's window is a run of consecutive positions on X, and the X
 // windows of the QB positions lie in the KW positions starting at the window of the first
 // one (KW = 32 for QB = 16, else 16; kx <= KW - QB + 1), so a key block of 32 keys holds
-// KW positions of 32 / KW rows. The workgroup walks the union of its rows' Y windows for
-// each t' of the common T window as such blocks, streamed through a four-slot LDS ring
+// KW positions of 32 / KW rows. The workgroup walks the union of its waves' Y windows for
+// each t' of the union of their T windows as such blocks, streamed through a four-slot LDS ring
 // exactly like the dense kernels stream key tiles; each block is copied once and used by
 // every wave whose rows' windows reach its rows:
 //
@@ -64,14 +65,16 @@ constexpr int kNaWaves = 4;  // waves per workgroup, stacked on Y
 // rows y, strip fastest; or (t_inner) t fastest, then strip, block of rows slowest,
 // which the host picks when a head has to be shared by several XCDs and cutting it
 // along Y or X duplicates fewer K/V rows than cutting it along T.
+// With tstack, t is the workgroup's block of four frames (the waves' t = 4 t + wave).
 __device__ __forceinline__ void na_decode(const NaParams& p, int& b, int& t, int& yblk,
                                           int& strip, int& h) {
     long idx = blockIdx.x;
     const long per = (long)gridDim.x >> 3;
     if (idx < (per << 3)) idx = (idx & 7) * per + (idx >> 3);
+    const int nt = p.tstack ? (p.T + kNaWaves - 1) / kNaWaves : p.T;
     if (p.t_inner) {
-        t = (int)(idx % p.T);
-        idx /= p.T;
+        t = (int)(idx % nt);
+        idx /= nt;
         strip = (int)(idx % p.strips);
         idx /= p.strips;
         yblk = (int)(idx % p.yblocks);
@@ -81,8 +84,8 @@ __device__ __forceinline__ void na_decode(const NaParams& p, int& b, int& t, int
         idx /= p.strips;
         yblk = (int)(idx % p.yblocks);
         idx /= p.yblocks;
-        t = (int)(idx % p.T);
-        idx /= p.T;
+        t = (int)(idx % nt);
+        idx /= nt;
     }
     h = (int)(idx % p.H);
     b = (int)(idx / p.H);
@@ -129,17 +132,21 @@ void attn_na3d_kernel(NaParams p) {
     const int n = lane & 31;
     const int g = lane >> 5;
 
-    int b, t, yblk, strip, h;
-    na_decode(p, b, t, yblk, strip, h);
+    int b, tb, yblk, strip, h;
+    na_decode(p, b, tb, yblk, strip, h);
 
+    // The workgroup's four waves: stacked on Y (QA rows each, one frame t), or with tstack
+    // on T (the same QA rows, frames 4 tb .. 4 tb + 3)
     const int X = p.X, Y = p.Y;
     const long HD = (long)p.H * D;
-    const int wy0 = yblk * YB + wave * QA;  // the wave's first row y
-    const bool active = wy0 < Y;
+    const int t = p.tstack ? kNaWaves * tb + wave : tb;                // the wave's frame
+    const int wy0 = p.tstack ? yblk * QA : yblk * YB + wave * QA;       // its first row y
+    const bool active = wy0 < Y && t < p.T;
     const int yq = wy0 + n / QB;            // this lane's query row
     const int xq = strip * QB + n % QB;     // and position on X
     const int yqc = min(yq, Y - 1), xqc = min(xq, X - 1);
-    const long pos_q = (((long)b * p.T + t) * Y + yqc) * X + xqc;
+    const int tqc = min(t, p.T - 1);
+    const long pos_q = (((long)b * p.T + tqc) * Y + yqc) * X + xqc;
 
     // Q^T fragments (B operand): lane holds query n, dims 16*ks + 8g .. +7
     bf16x8 qf[KS];
@@ -150,8 +157,8 @@ void attn_na3d_kernel(NaParams p) {
             qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks + 8 * g);
     }
 
-    // windows: T common to the workgroup, Y and X per query
-    const int t0 = na_start(t, p.kt, p.T);
+    // windows: T per wave (common to its queries), Y and X per query
+    const int tw0 = na_start(tqc, p.kt, p.T);
     const int ys_q = na_start(yqc, p.ky, Y);
     const int xs_q = na_start(xqc, p.kx, X);
     const int xa = na_start(strip * QB, p.kx, X);  // first key position of a block
@@ -162,10 +169,15 @@ void attn_na3d_kernel(NaParams p) {
     const int wv1 = na_start(wlast, p.ky, Y) + p.ky;
     const int wc0 = na_start(wlast, p.ky, Y);
     const int wc1 = wv0 + p.ky;
-    const int yu0 = na_start(min(yblk * YB, Y - 1), p.ky, Y);
-    const int yu1 = na_start(min(yblk * YB + YB - 1, Y - 1), p.ky, Y) + p.ky;
+    // the workgroup's union of windows: frames t' [tu0, tu1), rows y' [yu0, yu1)
+    const int ylast = p.tstack ? yblk * QA + QA - 1 : yblk * YB + YB - 1;
+    const int yu0 = na_start(min(p.tstack ? yblk * QA : yblk * YB, Y - 1), p.ky, Y);
+    const int yu1 = na_start(min(ylast, Y - 1), p.ky, Y) + p.ky;
+    const int tu0 = p.tstack ? na_start(min(kNaWaves * tb, p.T - 1), p.kt, p.T) : tw0;
+    const int tu1 = p.tstack ? na_start(min(kNaWaves * tb + kNaWaves - 1, p.T - 1), p.kt, p.T) + p.kt
+                             : tw0 + p.kt;
     const int nbr = (yu1 - yu0 + RPB - 1) / RPB;  // blocks per t'
-    const int nblocks = p.kt * nbr;
+    const int nblocks = (tu1 - tu0) * nbr;
 
     // Loader: thread tid copies physical chunk tid of a block: key j = tid / CPR (row
     // j / KW of the block, position xa + j % KW, clamped to the axis), position tid % CPR
@@ -185,7 +197,7 @@ void attn_na3d_kernel(NaParams p) {
     auto vslot = [&](int j) { return smem + j * 2 * TILEB + TILEB; };
     // block i: rows (t0 + i / nbr, yu0 + RPB * (i % nbr) ...) into slot i % NSLOT
     auto issue_block = [&](int i) {
-        const int tt = t0 + i / nbr, yy = yu0 + RPB * (i % nbr);
+        const int tt = tu0 + i / nbr, yy = yu0 + RPB * (i % nbr);
         const long rb = ((((long)b * p.T + tt) * Y + yy) * X * HD + (long)h * D) * 2;
         const unsigned off = (RPB == 1 || yy + 1 < Y) ? ld_off : ld_off1;
         load16_to_lds_sbase(kbase + rb, off, kslot(i % NSLOT) + wave * kWave * 16);
@@ -306,7 +318,8 @@ void attn_na3d_kernel(NaParams p) {
         barrier_tiles_left<AHEAD - 1>(nblocks - 1 - i);
         if (i + AHEAD < nblocks) issue_block(i + AHEAD);  // into the slot block i-1 left
         const int yy = yu0 + RPB * (i % nbr);
-        if (active && yy < wv1 && yy + RPB > wv0)
+        const int tt = tu0 + i / nbr;
+        if (active && yy < wv1 && yy + RPB > wv0 && tt >= tw0 && tt < tw0 + p.kt)
             compute(kslot(i % NSLOT), vslot(i % NSLOT), yy, yy < wc0 || yy + RPB > wc1);
     }
 
@@ -337,15 +350,30 @@ void na3d_configure(NaParams& p) {
     long best = -1;
     p.qb = 0;
     p.strips = p.yblocks = 0;  // no tile holds the window: nothing to launch
+    p.tstack = 0;
+    int qa = 0, rpb = 0;
     for (const Opt& o : opts) {
         if (p.kx > o.max_kx) continue;
         const long cost = (long)(o.qa + p.ky - 1) * o.kw;
         if (best < 0 || cost < best) {
             best = cost;
             p.qb = o.qb;
-            p.strips = (p.X + o.qb - 1) / o.qb;
-            p.yblocks = (p.Y + kNaWaves * o.qa - 1) / (kNaWaves * o.qa);
+            qa = o.qa;
+            rpb = 32 / o.kw;
         }
+    }
+    if (p.qb) {
+        // Stack the workgroup's four waves where they share more of their windows: on Y
+        // the workgroup walks the common T window over the union of 4 qa rows' Y windows,
+        // on T the union of four frames' T windows over qa rows' Y windows; a wave computes
+        // only the blocks in its own windows, so fewer block steps waste fewer barriers.
+        auto blocks_of = [&](int rows) { return (std::min(p.Y, rows + p.ky - 1) + rpb - 1) / rpb; };
+        const long steps_y = (long)p.kt * blocks_of(kNaWaves * qa);
+        const long steps_t = (long)std::min(p.T, p.kt + kNaWaves - 1) * blocks_of(qa);
+        p.tstack = steps_t < steps_y ? 1 : 0;
+        p.strips = (p.X + p.qb - 1) / p.qb;
+        const int rows = p.tstack ? qa : kNaWaves * qa;
+        p.yblocks = (p.Y + rows - 1) / rows;
     }
     // Heads shared by n XCDs are cut along the slowest axis of the order: T (t slowest),
     // else the blocks of rows y, or the strips when there is one block of rows. Each part
@@ -358,7 +386,8 @@ void na3d_configure(NaParams& p) {
             const double part = (double)len / n;
             return n * std::min((double)len, part + win - 1) / len;
         };
-        const double cut_t = p.T >= n ? dup(p.T, p.kt) : 1e30;
+        const int nt = p.tstack ? (p.T + kNaWaves - 1) / kNaWaves : p.T;  // units along T
+        const double cut_t = nt >= n ? dup(p.T, p.kt) : 1e30;
         const double cut_yx = p.yblocks >= n ? dup(p.Y, p.ky)
                               : (p.yblocks == 1 && p.strips >= n ? dup(p.X, p.kx) : 1e30);
         p.t_inner = cut_yx < cut_t ? 1 : 0;
@@ -366,7 +395,8 @@ void na3d_configure(NaParams& p) {
 }
 
 long long na3d_workgroups(const NaParams& p) {
-    return (long long)p.B * p.T * p.yblocks * p.strips * p.H;
+    const long long nt = p.tstack ? (p.T + kNaWaves - 1) / kNaWaves : p.T;
+    return (long long)p.B * nt * p.yblocks * p.strips * p.H;
 }
 
 hipError_t launch_na3d(const NaParams& p, hipStream_t stream) {
