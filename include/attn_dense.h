@@ -172,8 +172,8 @@ int attn_plan(int B, int Nq, int Nk, int H, int D, int num_splits, int waves, in
  * attn_na3d would return.
  *   query_cols: positions on X of a wavefront's query tile (16, 8 or 4; the tile is
  *               32 / query_cols rows y by query_cols positions), chosen per window
- *   workgroups: workgroups of the kernel (four wavefronts each, on four row tiles of one
- *               frame or on one row tile of four frames, whichever walks fewer key blocks)
+ *   workgroups: workgroups of the kernel (four wavefronts each: 1, 2 or 4 frames by 4, 2
+ *               or 1 row tiles, whichever walks the fewest key blocks)
  */
 int attn_na3d_plan(int B, int T, int Y, int X, int H, int D, int kt, int ky, int kx,
                    int* query_cols, long long* workgroups);

@@ -256,29 +256,37 @@ def test_na3d_plan_picks_a_tile_that_holds_the_window(window, cols):
     width = 32 if c == 16 else 16
     assert c - 1 + kx <= width
     rows = 32 // c
-    # four waves per workgroup, stacked on rows y (4 * rows rows of one frame) or on frames
-    # t (four frames of the same rows), whichever walks fewer key blocks: the union of the
-    # waves' windows, t' frames times blocks of 32 / width rows over the Y windows
-    def blocks(nrows):
-        return -(-min(Y, nrows + ky - 1) // (32 // width))
-    steps_y = kt * blocks(4 * rows)
-    steps_t = min(T, kt + 3) * blocks(rows)
-    if steps_t < steps_y:
-        expect = B * -(-T // 4) * -(-Y // rows) * -(-X // c) * H
-    else:
-        expect = B * T * -(-Y // (4 * rows)) * -(-X // c) * H
-    assert plan["workgroups"] == expect
+    assert plan["workgroups"] == na3d_grid(B, T, Y, X, H, window, c)
 
 
-def test_na3d_plan_stacks_waves_on_frames_where_windows_overlap_more():
-    """The four volumes of the pages' neighborhood definitions all walk fewer key blocks
-    with the waves on four frames: e.g. 3x7x7 on 64x64, 6 frames x 5 blocks against 3
-    frames x 11 blocks; 11x11x11 on 32x32, 14 x 9 against 11 x 16."""
-    for (T, Y, X, H, win) in [(8, 64, 64, 16, (3, 7, 7)), (8, 32, 32, 32, (3, 7, 7)),
-                              (16, 32, 32, 4, (11, 11, 11)), (8, 64, 64, 8, (3, 5, 5))]:
+def na3d_grid(B, T, Y, X, H, window, c):
+    """Four waves per workgroup, arranged as wt frames t by 4 / wt tiles of 32 / c rows,
+    wt in (1, 2, 4) walking the fewest key blocks: the union of the waves' windows, kt + wt - 1
+    frames times blocks of 32 / width rows over the union of their Y windows (ties to the
+    larger wt)."""
+    kt, ky, _ = window
+    rows = 32 // c
+    rpb = 32 // (32 if c == 16 else 16)
+    best = None
+    for wt in (1, 2, 4):
+        steps = min(T, kt + wt - 1) * -(-min(Y, 4 // wt * rows + ky - 1) // rpb)
+        if best is None or steps <= best[0]:
+            best = (steps, wt)
+    wt = best[1]
+    return B * -(-T // wt) * -(-Y // (4 // wt * rows)) * -(-X // c) * H
+
+
+def test_na3d_plan_arranges_waves_where_windows_overlap_most():
+    """The pages' four neighborhood volumes: 3x7x7 on 64x64 or 32x32 walks 28 blocks with
+    two frames by two row tiles (30 with four frames, 33 with four row tiles); 11x11x11 on
+    32x32 126 with four frames (156, 176); 3x5x5 on 64x64 24 with four frames (24, 30)."""
+    for (T, Y, X, H, win, wt) in [(8, 64, 64, 16, (3, 7, 7), 2), (8, 32, 32, 32, (3, 7, 7), 2),
+                                  (16, 32, 32, 4, (11, 11, 11), 4), (8, 64, 64, 8, (3, 5, 5), 4)]:
         plan = attn.attn_na3d_plan(1, T, Y, X, H, 64, *win)
         c = plan["query_cols"]
-        assert plan["workgroups"] == -(-T // 4) * -(-Y // (32 // c)) * -(-X // c) * H
+        rows = 32 // c
+        assert plan["workgroups"] == -(-T // wt) * -(-Y // (4 // wt * rows)) * -(-X // c) * H
+        assert plan["workgroups"] == na3d_grid(1, T, Y, X, H, win, c)
 
 
 def test_na3d_plan_errors_match_the_call():

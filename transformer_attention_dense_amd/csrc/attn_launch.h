@@ -54,9 +54,8 @@ struct NaParams {
     // set by na3d_configure: a wave's query tile (32 / qb rows y x qb positions on X)
     int qb;       // 16, 8 or 4
     int strips;   // ceil(X / qb): strips of qb positions on the X axis
-    int yblocks;  // blocks of rows y of a workgroup: ceil(Y / (4 * 32 / qb)), with tstack
-                  // ceil(Y / (32 / qb))
-    int tstack;   // the workgroup's four waves on four frames t (1) or on rows y (0)
+    int wt;       // frames t of a workgroup (1, 2 or 4), each with 4 / wt tiles of rows y
+    int yblocks;  // blocks of rows y of a workgroup: ceil(Y / (4 / wt * 32 / qb))
     int t_inner;  // workgroup order within a head (na_decode): t fastest (1) or slowest (0)
 };
 void na3d_configure(NaParams& p);

@@ -6,8 +6,8 @@
 // inside the axis at its ends).
 //
 // A wave owns 32 queries of one (b, t, h): QA rows y x QB positions on X (QB = 16, 8 or
-// 4, QA = 32 / QB, picked per window shape); a workgroup stacks four waves on Y, or on T
-// (four frames of the same rows) where their windows overlap more that way. Every
+// 4, QA = 32 / QB, picked per window shape); a workgroup holds four waves on 1, 2 or 4
+// frames t (4, 2 or 1 tiles of QA rows each), arranged where their windows overlap most. Every
 // (t', y') row of a query's window is a run of consecutive positions on X, and the X
 // windows of the QB positions lie in the KW positions starting at the window of the first
 // one (KW = 32 for QB = 16, else 16; kx <= KW - QB + 1), so a key block of 32 keys holds
@@ -56,22 +56,22 @@ __device__ __forceinline__ void barrier_tiles_left(int left) {
     }
 }
 
-constexpr int kNaWaves = 4;  // waves per workgroup, stacked on Y
+constexpr int kNaWaves = 4;  // waves per workgroup (frames x row tiles: na3d_configure)
 
-// Workgroup -> (b, t, block of YB rows y, strip of QB positions on X, h). Each XCD
+// Workgroup -> (b, block of frames t, block of rows y, strip of QB positions on X, h). Each XCD
 // (it runs the workgroups whose linear ids are equal mod 8) gets a contiguous range of
 // the order (b, h, ...), so the workgroups of a head, whose windows share K/V rows, run
 // on one XCD and meet the rows in its L2. Within a head: t slowest, then the block of
 // rows y, strip fastest; or (t_inner) t fastest, then strip, block of rows slowest,
 // which the host picks when a head has to be shared by several XCDs and cutting it
 // along Y or X duplicates fewer K/V rows than cutting it along T.
-// With tstack, t is the workgroup's block of four frames (the waves' t = 4 t + wave).
+// t is the workgroup's block of wt frames (its waves' frames wt t .. wt t + wt - 1).
 __device__ __forceinline__ void na_decode(const NaParams& p, int& b, int& t, int& yblk,
                                           int& strip, int& h) {
     long idx = blockIdx.x;
     const long per = (long)gridDim.x >> 3;
     if (idx < (per << 3)) idx = (idx & 7) * per + (idx >> 3);
-    const int nt = p.tstack ? (p.T + kNaWaves - 1) / kNaWaves : p.T;
+    const int nt = (p.T + p.wt - 1) / p.wt;
     if (p.t_inner) {
         t = (int)(idx % nt);
         idx /= nt;
@@ -121,7 +121,6 @@ void attn_na3d_kernel(NaParams p) {
     constexpr int NSLOT = 4;         // LDS ring slots
     constexpr int AHEAD = NSLOT - 1; // blocks copied ahead of the one in use
     constexpr int NPAIR = 8;         // exp pairs per lane per block
-    constexpr int YB = kNaWaves * QA;  // rows y per workgroup
     constexpr int NXM = KW == 16 ? 8 : 16;  // distinct X masks per lane
 
     __shared__ __attribute__((aligned(1024))) char smem[NSLOT * 2 * TILEB];
@@ -135,12 +134,13 @@ void attn_na3d_kernel(NaParams p) {
     int b, tb, yblk, strip, h;
     na_decode(p, b, tb, yblk, strip, h);
 
-    // The workgroup's four waves: stacked on Y (QA rows each, one frame t), or with tstack
-    // on T (the same QA rows, frames 4 tb .. 4 tb + 3)
+    // The workgroup's four waves: wt frames (wt tb ..) by 4 / wt tiles of QA rows (from row
+    // yblk * (4 / wt) * QA); wave w is frame w / (4 / wt), row tile w % (4 / wt)
     const int X = p.X, Y = p.Y;
     const long HD = (long)p.H * D;
-    const int t = p.tstack ? kNaWaves * tb + wave : tb;                // the wave's frame
-    const int wy0 = p.tstack ? yblk * QA : yblk * YB + wave * QA;       // its first row y
+    const int ay = kNaWaves / p.wt;                          // row tiles of the workgroup
+    const int t = p.wt * tb + wave / ay;                     // the wave's frame
+    const int wy0 = (yblk * ay + wave % ay) * QA;            // its first row y
     const bool active = wy0 < Y && t < p.T;
     const int yq = wy0 + n / QB;            // this lane's query row
     const int xq = strip * QB + n % QB;     // and position on X
@@ -170,12 +170,11 @@ void attn_na3d_kernel(NaParams p) {
     const int wc0 = na_start(wlast, p.ky, Y);
     const int wc1 = wv0 + p.ky;
     // the workgroup's union of windows: frames t' [tu0, tu1), rows y' [yu0, yu1)
-    const int ylast = p.tstack ? yblk * QA + QA - 1 : yblk * YB + YB - 1;
-    const int yu0 = na_start(min(p.tstack ? yblk * QA : yblk * YB, Y - 1), p.ky, Y);
+    const int yfirst = yblk * ay * QA, ylast = yfirst + ay * QA - 1;
+    const int yu0 = na_start(min(yfirst, Y - 1), p.ky, Y);
     const int yu1 = na_start(min(ylast, Y - 1), p.ky, Y) + p.ky;
-    const int tu0 = p.tstack ? na_start(min(kNaWaves * tb, p.T - 1), p.kt, p.T) : tw0;
-    const int tu1 = p.tstack ? na_start(min(kNaWaves * tb + kNaWaves - 1, p.T - 1), p.kt, p.T) + p.kt
-                             : tw0 + p.kt;
+    const int tu0 = na_start(min(p.wt * tb, p.T - 1), p.kt, p.T);
+    const int tu1 = na_start(min(p.wt * tb + p.wt - 1, p.T - 1), p.kt, p.T) + p.kt;
     const int nbr = (yu1 - yu0 + RPB - 1) / RPB;  // blocks per t'
     const int nblocks = (tu1 - tu0) * nbr;
 
@@ -350,7 +349,7 @@ void na3d_configure(NaParams& p) {
     long best = -1;
     p.qb = 0;
     p.strips = p.yblocks = 0;  // no tile holds the window: nothing to launch
-    p.tstack = 0;
+    p.wt = 1;
     int qa = 0, rpb = 0;
     for (const Opt& o : opts) {
         if (p.kx > o.max_kx) continue;
@@ -363,16 +362,22 @@ void na3d_configure(NaParams& p) {
         }
     }
     if (p.qb) {
-        // Stack the workgroup's four waves where they share more of their windows: on Y
-        // the workgroup walks the common T window over the union of 4 qa rows' Y windows,
-        // on T the union of four frames' T windows over qa rows' Y windows; a wave computes
-        // only the blocks in its own windows, so fewer block steps waste fewer barriers.
+        // Arrange the workgroup's four waves as wt frames by 4 / wt row tiles where they
+        // share the most of their windows: the workgroup walks the union of its waves' T
+        // windows (kt + wt - 1 frames) over the union of their Y windows (4 / wt tiles of
+        // qa rows, widened by ky - 1), and a wave computes only the blocks in its own
+        // windows, so fewer block steps waste fewer barriers. Ties go to more frames.
         auto blocks_of = [&](int rows) { return (std::min(p.Y, rows + p.ky - 1) + rpb - 1) / rpb; };
-        const long steps_y = (long)p.kt * blocks_of(kNaWaves * qa);
-        const long steps_t = (long)std::min(p.T, p.kt + kNaWaves - 1) * blocks_of(qa);
-        p.tstack = steps_t < steps_y ? 1 : 0;
+        long best_steps = -1;
+        for (int wt = 1; wt <= kNaWaves; wt *= 2) {
+            const long steps = (long)std::min(p.T, p.kt + wt - 1) * blocks_of(kNaWaves / wt * qa);
+            if (best_steps < 0 || steps <= best_steps) {
+                best_steps = steps;
+                p.wt = wt;
+            }
+        }
         p.strips = (p.X + p.qb - 1) / p.qb;
-        const int rows = p.tstack ? qa : kNaWaves * qa;
+        const int rows = kNaWaves / p.wt * qa;
         p.yblocks = (p.Y + rows - 1) / rows;
     }
     // Heads shared by n XCDs are cut along the slowest axis of the order: T (t slowest),
@@ -386,7 +391,7 @@ void na3d_configure(NaParams& p) {
             const double part = (double)len / n;
             return n * std::min((double)len, part + win - 1) / len;
         };
-        const int nt = p.tstack ? (p.T + kNaWaves - 1) / kNaWaves : p.T;  // units along T
+        const int nt = (p.T + p.wt - 1) / p.wt;  // units along T
         const double cut_t = nt >= n ? dup(p.T, p.kt) : 1e30;
         const double cut_yx = p.yblocks >= n ? dup(p.Y, p.ky)
                               : (p.yblocks == 1 && p.strips >= n ? dup(p.X, p.kx) : 1e30);
@@ -395,7 +400,7 @@ void na3d_configure(NaParams& p) {
 }
 
 long long na3d_workgroups(const NaParams& p) {
-    const long long nt = p.tstack ? (p.T + kNaWaves - 1) / kNaWaves : p.T;
+    const long long nt = (p.T + p.wt - 1) / p.wt;
     return (long long)p.B * nt * p.yblocks * p.strips * p.H;
 }
 
