@@ -370,18 +370,20 @@ def check_na3d_full_size(w, ts, idx):
 
 NA_CASES = [
     # (B, T, Y, X, H, (kt, ky, kx)); the wave tile the library picks (rows y x positions
-    # on X) in brackets
-    (1, 3, 5, 7, 4, (3, 3, 5)),      # [4x8] one strip; windows moved inside at every border
-    (2, 4, 6, 40, 3, (3, 5, 7)),     # [4x8] five strips; two idle waves
-    (1, 5, 9, 33, 5, (5, 7, 11)),    # [8x4] a one-query strip; a block past the Y axis
-    (1, 2, 3, 64, 8, (1, 3, 1)),     # [4x8] windows of one position on T and X
-    (1, 1, 2, 35, 2, (1, 1, 17)),    # [2x16] the widest X window
-    (1, 3, 11, 19, 3, (3, 9, 17)),   # [2x16] widest X window, wave rows split by Y windows
-    (1, 2, 21, 24, 2, (1, 5, 13)),   # [2x16] three blocks of rows y, one of them interior
-    (1, 3, 37, 30, 2, (3, 9, 11)),   # [8x4] ragged blocks of rows y and strips
-    (1, 2, 9, 20, 3, (1, 3, 5)),     # [4x8] the last key block's second row past the Y axis
-    (1, 3, 3, 3, 4, (3, 3, 3)),      # [4x8] the window covers the volume
-    (1, 2, 4, 97, 4, (1, 3, 9)),     # [4x8] 13 strips, the last one query wide
+    # on X) and the workgroup's arrangement (frames x row tiles) in brackets
+    (1, 3, 5, 7, 4, (3, 3, 5)),      # [4x8 4x1] one strip; windows moved inside at every border
+    (2, 4, 6, 40, 3, (3, 5, 7)),     # [4x8 1x4] five strips; two idle waves
+    (1, 7, 19, 24, 2, (3, 7, 5)),    # [4x8 2x2] the last frame pair's second frame past T
+    (1, 6, 33, 21, 2, (3, 9, 9)),    # [4x8 2x2] a row tile of one row; a one-query strip
+    (1, 5, 9, 33, 5, (5, 7, 11)),    # [8x4 4x1] a one-query strip; a block past the Y axis
+    (1, 2, 3, 64, 8, (1, 3, 1)),     # [4x8 1x4] windows of one position on T and X
+    (1, 1, 2, 35, 2, (1, 1, 17)),    # [2x16 4x1] the widest X window; three frames past T
+    (1, 3, 11, 19, 3, (3, 9, 17)),   # [2x16 4x1] widest X window, wave rows split by Y windows
+    (1, 2, 21, 24, 2, (1, 5, 13)),   # [2x16 4x1] eleven row tiles, most of them interior
+    (1, 3, 37, 30, 2, (3, 9, 11)),   # [8x4 4x1] ragged row tiles and strips
+    (1, 2, 9, 20, 3, (1, 3, 5)),     # [4x8 1x4] the last key block's second row past the Y axis
+    (1, 3, 3, 3, 4, (3, 3, 3)),      # [4x8 4x1] the window covers the volume
+    (1, 2, 4, 97, 4, (1, 3, 9)),     # [4x8 1x4] 13 strips, the last one query wide
 ]
 
 
