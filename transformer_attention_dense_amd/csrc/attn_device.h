@@ -97,6 +97,9 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 // 16-byte global -> LDS copy (global_load_lds_dwordx4). Lane i of the wave writes
 // LDS bytes [dst + 16*i, dst + 16*i + 16); dst must be the same for the whole wave.
+// NT marks the load non-temporal: for bytes no other workgroup reads, so the caches do
+// not keep them at the expense of data that is shared.
+template <bool NT = false>
 __device__ __forceinline__ void load16_to_lds(const uint16_t* src, char* dst) {
     // Issued as inline assembly on purpose: the compiler cannot tell which LDS bytes an
     // LDS-DMA copy writes, so for the builtin it waits for every copy in flight before
@@ -110,13 +113,22 @@ __device__ __forceinline__ void load16_to_lds(const uint16_t* src, char* dst) {
     // M0 is clobbered on purpose: nothing else in these kernels keeps a value in it.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-    __asm__ volatile(
-        "s_mov_b32 m0, %1\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %0, off"
-        :
-        : "v"(src), "s"(lds)
-        : "memory", "m0");
+    if constexpr (NT)
+        __asm__ volatile(
+            "s_mov_b32 m0, %1\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %0, off nt"
+            :
+            : "v"(src), "s"(lds)
+            : "memory", "m0");
+    else
+        __asm__ volatile(
+            "s_mov_b32 m0, %1\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %0, off"
+            :
+            : "v"(src), "s"(lds)
+            : "memory", "m0");
 #pragma clang diagnostic pop
 }
 
@@ -132,19 +144,29 @@ __device__ __forceinline__ uint64_t uniform_u64(uint64_t a) {
 // The same copy with a wave-uniform base address and a per-lane 32-bit byte offset:
 // the load adds them itself (scalar-base form), so issuing it takes no vector
 // instructions. base must be the same for the whole wave.
+template <bool NT = false>
 __device__ __forceinline__ void load16_to_lds_sbase(const void* base, unsigned voff, char* dst) {
     const unsigned lds = __builtin_amdgcn_readfirstlane(
         (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)dst);
     const uint64_t sb = uniform_u64((uint64_t)(uintptr_t)base);
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-    __asm__ volatile(
-        "s_mov_b32 m0, %2\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %0, %1"
-        :
-        : "v"(voff), "s"(sb), "s"(lds)
-        : "memory", "m0");
+    if constexpr (NT)
+        __asm__ volatile(
+            "s_mov_b32 m0, %2\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %0, %1 nt"
+            :
+            : "v"(voff), "s"(sb), "s"(lds)
+            : "memory", "m0");
+    else
+        __asm__ volatile(
+            "s_mov_b32 m0, %2\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %0, %1"
+            :
+            : "v"(voff), "s"(sb), "s"(lds)
+            : "memory", "m0");
 #pragma clang diagnostic pop
 }
 
@@ -194,7 +216,7 @@ __device__ __forceinline__ void barrier_vmcnt() {
 //
 // Copy in: global -> LDS (global_load_lds_dwordx4, D/16 copies per lane); the caller
 // waits for them (vmcnt) before reading the rows.
-template <int D>
+template <int D, bool NT = false>
 __device__ __forceinline__ void copy_wave_rows_to_lds(const uint16_t* base, long stride,
                                                       int nvalid, char* rows) {
     constexpr int CPR = D / 8;
@@ -204,7 +226,7 @@ __device__ __forceinline__ void copy_wave_rows_to_lds(const uint16_t* base, long
         const int id = i * kWave + lane;
         const int r = id / CPR;
         const int lc = (id % CPR) ^ lds_swizzle<CPR>(r);
-        load16_to_lds(base + (long)min(r, nvalid - 1) * stride + lc * 8, rows + i * kWave * 16);
+        load16_to_lds<NT>(base + (long)min(r, nvalid - 1) * stride + lc * 8, rows + i * kWave * 16);
     });
 }
 
@@ -256,7 +278,8 @@ __device__ __forceinline__ void store_wave_rows_via_lds_to(const f32x16 (&o)[D /
     });
 }
 
-// The same for rows `stride` elements apart from base, of which the first nvalid exist.
+// The same for rows `stride` elements apart from base, of which the first nvalid exist;
+// the stores are non-temporal (the output is not read again by the kernel).
 template <int D>
 __device__ __forceinline__ void store_wave_rows_via_lds(const f32x16 (&o)[D / 32], float inv,
                                                         char* rows, uint16_t* base,
@@ -285,7 +308,7 @@ __device__ __forceinline__ void store_wave_rows_via_lds(const f32x16 (&o)[D / 32
         const int pc = id % CPR;
         const u32x4 v = *reinterpret_cast<const u32x4*>(rows + r * 2 * D + 16 * pc);
         if (r < nvalid)
-            *reinterpret_cast<u32x4*>(base + (long)r * stride + (pc ^ lds_swizzle<CPR>(r)) * 8) = v;
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(base + (long)r * stride + (pc ^ lds_swizzle<CPR>(r)) * 8));
     });
 }
 

@@ -135,7 +135,9 @@ __global__ __launch_bounds__(NW* kWave) __attribute__((amdgpu_waves_per_eu(
         ld_off[i] = r * HD + c * 8;
     }
 
-    auto issue = [&](const uint16_t* seg0, const uint16_t* seg1, int t0, char* slot) {
+    // nt_c: non-temporal copies (a tile no other workgroup reads)
+    auto issue = [&](const uint16_t* seg0, const uint16_t* seg1, int t0, char* slot, auto nt_c) {
+        constexpr bool NTL = decltype(nt_c)::value;
         char* const dst = slot + wave * kWave * 16;
         const bool whole = (t0 + BN <= kend) && (t0 + BN <= n0 || t0 >= n0);
         if (whole) {
@@ -143,8 +145,8 @@ __global__ __launch_bounds__(NW* kWave) __attribute__((amdgpu_waves_per_eu(
             const uint16_t* base = ((t0 < n0) ? seg0 : seg1) + rowoff;
 #pragma unroll
             for (int i = 0; i < PER_T; ++i)  // uniform base, per-lane offset
-                load16_to_lds_sbase(base + (long)(i / NPAT) * NPAT * RSTEP * HD,
-                                    2u * ld_off[i % NPAT], dst + i * NT * 16);
+                load16_to_lds_sbase<NTL>(base + (long)(i / NPAT) * NPAT * RSTEP * HD,
+                                         2u * ld_off[i % NPAT], dst + i * NT * 16);
         } else {
             // ragged or segment-straddling tile: clamp rows into [t0, kend) and pick
             // the segment per row
@@ -155,13 +157,15 @@ __global__ __launch_bounds__(NW* kWave) __attribute__((amdgpu_waves_per_eu(
                 const int co = ld_off[i % NPAT] - (r - (i / NPAT) * NPAT * RSTEP) * HD;
                 const uint16_t* src =
                     key < n0 ? seg0 + (long)key * HD : seg1 + (long)(key - n0) * HD;
-                load16_to_lds(src + co, dst + i * NT * 16);
+                load16_to_lds<NTL>(src + co, dst + i * NT * 16);
             }
         }
     };
-    auto issue_k = [&](int t0, int slot) { issue(kseg0, kseg1, t0, smem + slot * TILEB); };
+    auto issue_k = [&](int t0, int slot) {
+        issue(kseg0, kseg1, t0, smem + slot * TILEB, std::false_type{});
+    };
     auto issue_v = [&](int t0, int slot) {
-        issue(vseg0, vseg1, t0, smem + (NSLOT + slot) * TILEB);
+        issue(vseg0, vseg1, t0, smem + (NSLOT + slot) * TILEB, std::false_type{});
     };
 
     // Per-lane LDS byte offsets of the K operand reads (per k-step) and of the V
@@ -353,10 +357,21 @@ __global__ __launch_bounds__(NW* kWave) __attribute__((amdgpu_waves_per_eu(
     auto kslot = [&](int j) { return smem + (j % NSLOT) * TILEB; };
     auto vslot = [&](int j) { return smem + (NSLOT + j % NSLOT) * TILEB; };
     if constexpr (NSLOT == 1) {
-        // every key range of the call is one tile (the launcher checks it)
-        copy_wave_rows_to_lds<D>(p.q + qrow0, HD, p.Nq - q0, qo);
-        issue_k(kbeg, 0);
-        issue_v(kbeg, 0);
+        // every key range of the call is one tile (the launcher checks it). The copies
+        // of what only this workgroup reads are non-temporal: its Q rows when the keys
+        // are not split, its K and V tile when a (batch, head) has one query block
+        // (B=1024 N=64: 185.7 -> 168.1 us with the non-temporal output stores).
+        if (p.splits == 1)
+            copy_wave_rows_to_lds<D, true>(p.q + qrow0, HD, p.Nq - q0, qo);
+        else
+            copy_wave_rows_to_lds<D>(p.q + qrow0, HD, p.Nq - q0, qo);
+        if (p.m_blocks == 1) {
+            issue(kseg0, kseg1, kbeg, smem, std::true_type{});
+            issue(vseg0, vseg1, kbeg, smem + TILEB, std::true_type{});
+        } else {
+            issue_k(kbeg, 0);
+            issue_v(kbeg, 0);
+        }
         barrier_vmcnt<0>();
         if (active) {
             read_wave_rows_qf<D>(qo, qf);
