@@ -141,7 +141,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // Q^T fragments (B operand): lane holds query n, dims 16*ks + 8g .. +7.
     // They arrive through the wave's LDS rows (below): lane i of round r copies 16-byte
     // chunk 64 r + i of the wave's 32 rows, swizzled like the K/V rows, so each copy
-    // instruction covers whole rows rather than 32 bytes of 32 rows.
+    // instruction covers whole rows rather than 32 bytes of 32 rows. Without a key split no
+    // other workgroup reads these rows, so they take the non-temporal path and leave L2 to
+    // the K/V tiles that every query tile of the head re-reads.
     bf16x8 qf[KS];
     char* const qo = smem + 2 * NSLOT * TILEB + wave * WB;
     auto issue_q = [&]() {
@@ -151,8 +153,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const int r = id / CPR;
             const int lc = (id % CPR) ^ lds_swizzle<CPR>(r);
             const int qi = min(q0 + r, p.Nq - 1);
-            load16_to_lds(p.q + ((long)(b * p.Nq + qi) * H + h) * D + lc * 8,
-                          qo + i * kWave * 16);
+            const uint16_t* const src = p.q + ((long)(b * p.Nq + qi) * H + h) * D + lc * 8;
+            if (p.splits == 1)
+                load16_to_lds<true>(src, qo + i * kWave * 16);
+            else
+                load16_to_lds(src, qo + i * kWave * 16);
         });
     };
 
@@ -558,7 +563,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int qi = q0 + n;
     if (p.splits == 1) {
         // The output rows go out through the wave's LDS rows so that each store covers
-        // whole rows (16 or 8 lanes per row) rather than 8 bytes of 32 rows.
+        // whole rows (16 or 8 lanes per row) rather than 8 bytes of 32 rows; nothing here
+        // reads them again, so the stores are non-temporal.
         char* const stage = qo;
         const float inv = 1.0f / l_tot;
         const int sw = lds_swizzle<CPR>(n);
@@ -580,10 +586,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const int id = i * kWave + lane;
             const int r = id / CPR;
             const int pc = id % CPR;
-            const uint4 v = *reinterpret_cast<const uint4*>(stage + r * ROWB + 16 * pc);
+            const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * ROWB + 16 * pc);
             if (q0 + r < p.Nq)
-                *reinterpret_cast<uint4*>(p.out + ((long)(b * p.Nq + q0 + r) * H + h) * D +
-                                          (pc ^ lds_swizzle<CPR>(r)) * 8) = v;
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p.out + ((long)(b * p.Nq + q0 + r) * H + h) * D +
+                                          (pc ^ lds_swizzle<CPR>(r)) * 8));
         });
     } else {
         const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
