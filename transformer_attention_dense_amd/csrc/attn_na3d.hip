@@ -19,9 +19,9 @@
 //   * copy the K and V block (global_load_lds_dwordx4, scalar base + per-lane offsets
 //     fixed for the workgroup; positions past the end of the X axis are clamped and never
 //     visible), three blocks ahead of their use;
-//   * S^T = K Q^T with 32x32x16 BF16 MFMAs (S in FP32); per lane, keys outside its
-//     query's X window get -inf added, and keys of rows outside its Y window too where
-//     the block is not inside every Y window of the wave;
+//   * S^T = K Q^T with 32x32x16 BF16 MFMAs (S in FP32), accumulated onto a per-lane
+//     0/-inf mask of the keys outside its query's X window; keys of rows outside its Y
+//     window get -inf added where the block is not inside every Y window of the wave;
 //   * online softmax in the exp2 domain (scale 1, so c = log2 e), P rounded to BF16;
 //   * O^T += V^T P^T with the V operand read transposed from LDS (ds_read_b64_tr_b16).
 #include <hip/hip_runtime.h>
@@ -121,7 +121,6 @@ void attn_na3d_kernel(NaParams p) {
     constexpr int NSLOT = 4;         // LDS ring slots
     constexpr int AHEAD = NSLOT - 1; // blocks copied ahead of the one in use
     constexpr int NPAIR = 8;         // exp pairs per lane per block
-    constexpr int NXM = KW == 16 ? 8 : 16;  // distinct X masks per lane
 
     __shared__ __attribute__((aligned(1024))) char smem[NSLOT * 2 * TILEB];
 
@@ -236,11 +235,11 @@ void attn_na3d_kernel(NaParams p) {
 
     // Score register r of a lane holds key j = 8 (r / 4) + 4 g + r % 4 of the block: row
     // j / KW, position xa + j % KW. The X window of a query covers the same keys of every
-    // block: keys outside it get -inf added (registers r and r + 8 share a position when
-    // KW = 16).
-    float xm[NXM];
+    // block: the score accumulators start at -inf for the keys outside it (registers r
+    // and r + 8 share a position when KW = 16), so the mask costs no instruction per block.
+    f32x16 xm;
 #pragma unroll
-    for (int r = 0; r < NXM; ++r) {
+    for (int r = 0; r < 16; ++r) {
         const int xk = xa + (8 * (r >> 2) + 4 * g + (r & 3)) % KW;
         xm[r] = (xk < xs_q || xk >= xs_q + p.kx) ? -INFINITY : 0.f;
     }
@@ -248,16 +247,13 @@ void attn_na3d_kernel(NaParams p) {
     // One block; ymask when some of its rows lie outside the Y window of some query of
     // the wave (those rows' keys get -inf for that query). ymask is uniform.
     auto compute = [&](const char* kt_lds, const char* vt_lds, int yy, bool ymask) {
-        // ---- S^T = K Q^T
-        f32x16 s = f32x16{};
+        // ---- S^T = K Q^T, onto the X window mask
+        f32x16 s = xm;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt_lds + koff[ks]);
             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s, 0, 0, 0);
         }
-        // ---- keys outside the query's window are hidden
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] += xm[r % NXM];
         if (ymask) {
 #pragma unroll
             for (int hr = 0; hr < RPB; ++hr) {
@@ -313,6 +309,10 @@ void attn_na3d_kernel(NaParams p) {
     // barrier before block i waits for its copies and lets the later ones stay in flight
     const int npre = min(AHEAD, nblocks);
     for (int i = 0; i < npre; ++i) issue_block(i);
+    // Q is resident before the loop (with the first blocks): a wait the compiler sees, so
+    // it puts none for the Q registers inside the loop, where the hardware count would
+    // also take in the block copies just issued and expose their latency on every step.
+    __builtin_amdgcn_s_waitcnt((0) | (0 << 14) | (7 << 4) | (15 << 8));  // vmcnt(0)
     for (int i = 0; i < nblocks; ++i) {
         barrier_tiles_left<AHEAD - 1>(nblocks - 1 - i);
         if (i + AHEAD < nblocks) issue_block(i + AHEAD);  // into the slot block i-1 left
