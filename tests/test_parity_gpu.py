@@ -401,6 +401,21 @@ def test_na3d_small_all_elements(case):
     assert_accepted(host(out).reshape(-1, 64), ref.reshape(-1, 64), f"na3d {case}")
 
 
+def test_na3d_large_logits_rescale_across_blocks():
+    """Logits with a spread of hundreds (Q scaled by 6, K by 2: score sd about 96) raise
+    the running maximum many times over a query's blocks; two batches, the 2x2 workgroup
+    arrangement."""
+    shape = (2, 4, 13, 22, 2, 64)
+    kernel = (3, 7, 5)
+    say(f"na3d large logits {shape} {kernel}")
+    q = synth.normal_bf16(shape, 1700, 6.0)
+    k = synth.normal_bf16(shape, 1701, 2.0)
+    v = synth.normal_bf16(shape, 1702, 1.0)
+    out = attn.na3d(dev(q), dev(k), dev(v), kernel)
+    ref = oracle.na3d_attention(q, k, v, kernel)
+    assert_accepted(host(out).reshape(-1, 64), ref.reshape(-1, 64), "na3d large logits")
+
+
 def test_na3d_writes_only_its_output():
     shape = (1, 2, 3, 40, 4, 64)
     q, k, v = (dev(synth.normal_bf16(shape, 1600 + i, 1.0)) for i in range(3))
