@@ -69,7 +69,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     static_assert(D == 64 || D == 128, "head dim");
     constexpr int NW = 8;
     constexpr int NT = NW * kWave;
-    constexpr int BN = 64;  // keys per tile (a multiple of 32)
+    // keys per tile (a multiple of 32): 128 at D = 64, so a phase holds as many MFMAs as at
+    // D = 128 and the barriers per key halve (4-6% faster); the block-causal form keeps 64,
+    // the granularity of its key ends
+    constexpr int BN = (D == 64 && !BC) ? 128 : 64;
     constexpr int NB = BN / 32;            // 32-key blocks per tile
     constexpr int KS = D / 16;             // MFMA k-steps over the head dim
     constexpr int DB = D / 32;             // 32-wide head-dim blocks of O^T
@@ -377,12 +380,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 return;
             }
         } else if (t0 + BN > kend) {
+            // register r of block kb holds key t0 + 32 kb + 8 (r / 4) + 4 g + r % 4; the
+            // keys from kend on get -inf by bit selection against one per-lane limit (no
+            // per-register offsets or compare masks to keep live)
+            const int lim = kend - t0 - 4 * g;
 #pragma unroll
             for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int key = t0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-                    if (key >= kend) s[kb][r] = -INFINITY;
+                    const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
+                    const int hide = (lim - off - 1) >> 31;  // all ones when off >= lim
+                    s[kb][r] = __int_as_float((__float_as_int(s[kb][r]) & ~hide) |
+                                              (int)(0xff800000u & (unsigned)hide));
                 }
         }
         if (lazy_ok) {
