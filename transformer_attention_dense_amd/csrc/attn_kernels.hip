@@ -44,18 +44,21 @@ namespace {
 
 using namespace dev;
 
-// Waves per SIMD the kernel is compiled for: two with an LDS ring (registers for two
-// score buffers); a call whose key ranges fit one tile (NSLOT = 1) needs one score
-// buffer and no ring: three at D = 64, where the LDS (K, V, and the query rows) still
-// holds six two-wave workgroups per CU.
-template <int D, int NSLOT>
+// Waves per SIMD the kernel is compiled for, at D = 64 three: a call whose key ranges fit
+// one tile (NSLOT = 1) needs one score buffer and no ring, and the LDS (K, V, and the
+// query rows) still holds six two-wave workgroups per CU; the four-wave ring form fits
+// 168 VGPRs (one spilled) and three workgroups per CU (48 KiB of ring each), which took
+// 10-13% off grids of thousands of short query blocks (B=64 N=128 H=32: 25.8 -> 23.2 us;
+// B=32 N=200: 33.8 -> 29.5) and left grids of one or two workgroups per CU unchanged.
+// Otherwise two (registers for two score buffers).
+template <int D, int NW, int NSLOT>
 constexpr int fwd_waves_per_simd() {
-    return (NSLOT == 1 && D == 64) ? 3 : 2;
+    return (D == 64 && (NSLOT == 1 || NW == 4)) ? 3 : 2;
 }
 
 template <int D, int NW, int BN, int NSLOT>
 __global__ __launch_bounds__(NW* kWave) __attribute__((amdgpu_waves_per_eu(
-    fwd_waves_per_simd<D, NSLOT>(), fwd_waves_per_simd<D, NSLOT>()))) void attn_fwd_kernel(FwdParams p) {
+    fwd_waves_per_simd<D, NW, NSLOT>(), fwd_waves_per_simd<D, NW, NSLOT>()))) void attn_fwd_kernel(FwdParams p) {
     static_assert(D == 64 || D == 128, "head dim");
     static_assert(BN % 32 == 0 && BN <= 128, "key tile");
     static_assert(NSLOT >= 1 && NSLOT <= 3, "LDS ring depth (1: one tile per workgroup)");
