@@ -426,6 +426,74 @@ def test_na3d_writes_only_its_output():
     assert bool((big[:q.numel()] == 7.0).all()) and bool((big[2 * q.numel():] == 7.0).all())
 
 
+# ---------------------------------------------------------------- tensors of 2^31 elements
+
+def need_free_gib(gib):
+    free = torch.cuda.mem_get_info()[0]
+    if free < gib * 2**30:
+        pytest.skip(f"needs {gib} GiB of free device memory, {free / 2**30:.1f} GiB free")
+
+
+def batched_copies(one_shape, B, seeds_first, seeds_last, sigmas):
+    """Three device tensors of B batches: batch 0 and batch B - 1 from seeded inputs of
+    their own, the batches between copies of batch 0. Also returns the host bits of the
+    first and the last batch."""
+    first = [synth.normal_bf16(one_shape, s, sg) for s, sg in zip(seeds_first, sigmas)]
+    last = [synth.normal_bf16(one_shape, s, sg) for s, sg in zip(seeds_last, sigmas)]
+    full = (B,) + tuple(one_shape[1:])
+    ts = []
+    for f, l in zip(first, last):
+        t = torch.empty(full, dtype=torch.bfloat16, device="cuda")
+        t[:-1].copy_(dev(f).expand((B - 1,) + tuple(one_shape[1:])))
+        t[-1:].copy_(dev(l))
+        ts.append(t)
+    return ts, first, last
+
+
+def middle_batches_match_first(out):
+    bits = out.view(torch.int16)
+    return bool((bits[1:-1] == bits[:1]).all())
+
+
+def test_dense_tensors_of_2_pow_31_elements():
+    """B=128 N=4096 H=32 D=128: 2^31 elements (4 GiB) per tensor, so offsets past one
+    batch need 64 bits. Sampled rows of the first and the last batch (inputs of their
+    own) against the oracle; the batches between (copies of the first) bit-identical to
+    it."""
+    B, N, H, D = 128, 4096, 32, 128
+    need_free_gib(24)
+    say(f"dense B{B} N{N} H{H} D{D}: 2^31 elements per tensor")
+    (q, k, v), first, last = batched_copies((1, N, H, D), B, (1800, 1801, 1802),
+                                            (1810, 1811, 1812), (1.0, 1.0, 1.0))
+    out = attn.dense(q, k, v)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(1820).choice(N * H, 512, replace=False))
+    for b, src in ((0, first), (B - 1, last)):
+        got = host(out[b]).reshape(-1, D)[rows]
+        ref = oracle.attention_rows(*src, rows=rows)
+        say(f"dense 2^31 batch {b}: {assert_accepted(got, ref, f'dense 2^31 batch {b}')}")
+    assert middle_batches_match_first(out)
+
+
+def test_na3d_tensors_of_2_pow_31_elements():
+    """B=64 T=8 Y=64 X=64 H=16 D=64, window 3x7x7: 2^31 elements per tensor, checked as
+    the dense case above."""
+    B, T, Y, X, H, D = 64, 8, 64, 64, 16, 64
+    kernel = (3, 7, 7)
+    need_free_gib(24)
+    say(f"na3d B{B} T{T} Y{Y} X{X} H{H} D{D} {kernel}: 2^31 elements per tensor")
+    (q, k, v), first, last = batched_copies((1, T, Y, X, H, D), B, (1830, 1831, 1832),
+                                            (1840, 1841, 1842), (0.125, 1.0, 1.0))
+    out = attn.na3d(q, k, v, kernel)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(1850).choice(T * Y * X * H, 512, replace=False))
+    for b, src in ((0, first), (B - 1, last)):
+        got = host(out[b]).reshape(-1, D)[rows]
+        ref = oracle.na3d_rows(*src, kernel, rows=rows)
+        say(f"na3d 2^31 batch {b}: {assert_accepted(got, ref, f'na3d 2^31 batch {b}')}")
+    assert middle_batches_match_first(out)
+
+
 # ---------------------------------------------------------------- streams
 
 def test_calls_run_on_the_current_stream():
