@@ -193,13 +193,25 @@ void attn_na3d_kernel(NaParams p) {
     const char* vbase = reinterpret_cast<const char*>(uniform_ptr(p.v));
     auto kslot = [&](int j) { return smem + j * 2 * TILEB; };
     auto vslot = [&](int j) { return smem + j * 2 * TILEB + TILEB; };
-    // block i: rows (t0 + i / nbr, yu0 + RPB * (i % nbr) ...) into slot i % NSLOT
-    auto issue_block = [&](int i) {
-        const int tt = tu0 + i / nbr, yy = yu0 + RPB * (i % nbr);
-        const long rb = ((((long)b * p.T + tt) * Y + yy) * X * HD + (long)h * D) * 2;
-        const unsigned off = (RPB == 1 || yy + 1 < Y) ? ld_off : ld_off1;
-        load16_to_lds_sbase(kbase + rb, off, kslot(i % NSLOT) + wave * kWave * 16);
-        load16_to_lds_sbase(vbase + rb, off, vslot(i % NSLOT) + wave * kWave * 16);
+    // Block i covers rows (tu0 + i / nbr, yu0 + RPB * (i % nbr) ...) and goes to slot
+    // i % NSLOT. Two cursors walk the blocks in order (the copies AHEAD blocks in front of
+    // the computation), so no step divides by nbr or multiplies out a row address.
+    const long rowb = (long)X * HD * 2;  // bytes per row y of one frame
+    const long bh0 = ((long)b * p.T * Y * X * HD + (long)h * D) * 2;
+    const int yend = yu0 + nbr * RPB;
+    int cp_t = tu0, cp_y = yu0;                          // next block to copy
+    long cp_rb = bh0 + ((long)tu0 * Y + yu0) * rowb;
+    auto issue_next = [&](int slot) {
+        const unsigned off = (RPB == 1 || cp_y + 1 < Y) ? ld_off : ld_off1;
+        load16_to_lds_sbase(kbase + cp_rb, off, kslot(slot) + wave * kWave * 16);
+        load16_to_lds_sbase(vbase + cp_rb, off, vslot(slot) + wave * kWave * 16);
+        cp_y += RPB;
+        cp_rb += RPB * rowb;
+        if (cp_y == yend) {
+            cp_y = yu0;
+            ++cp_t;
+            cp_rb = bh0 + ((long)cp_t * Y + yu0) * rowb;
+        }
     };
 
     // Per-lane LDS byte offsets: K operand reads per k-step, V transpose reads per
@@ -308,18 +320,22 @@ void attn_na3d_kernel(NaParams p) {
     // ---- pipeline: block i is copied AHEAD blocks ahead into slot i % NSLOT; the
     // barrier before block i waits for its copies and lets the later ones stay in flight
     const int npre = min(AHEAD, nblocks);
-    for (int i = 0; i < npre; ++i) issue_block(i);
+    for (int i = 0; i < npre; ++i) issue_next(i % NSLOT);
     // Q is resident before the loop (with the first blocks): a wait the compiler sees, so
     // it puts none for the Q registers inside the loop, where the hardware count would
     // also take in the block copies just issued and expose their latency on every step.
     __builtin_amdgcn_s_waitcnt((0) | (0 << 14) | (7 << 4) | (15 << 8));  // vmcnt(0)
+    int tt = tu0, yy = yu0;  // the block computed
     for (int i = 0; i < nblocks; ++i) {
         barrier_tiles_left<AHEAD - 1>(nblocks - 1 - i);
-        if (i + AHEAD < nblocks) issue_block(i + AHEAD);  // into the slot block i-1 left
-        const int yy = yu0 + RPB * (i % nbr);
-        const int tt = tu0 + i / nbr;
+        if (i + AHEAD < nblocks) issue_next((i + AHEAD) % NSLOT);  // the slot block i-1 left
         if (active && yy < wv1 && yy + RPB > wv0 && tt >= tw0 && tt < tw0 + p.kt)
             compute(kslot(i % NSLOT), vslot(i % NSLOT), yy, yy < wc0 || yy + RPB > wc1);
+        yy += RPB;
+        if (yy == yend) {
+            yy = yu0;
+            ++tt;
+        }
     }
 
     // ---- epilogue
