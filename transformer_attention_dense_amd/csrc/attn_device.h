@@ -95,6 +95,13 @@ __device__ __forceinline__ void static_for(F&& f) {
     static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
+// LDS byte address of a generic pointer into LDS: its low 32 bits (the flat aperture
+// of the LDS is 4 GiB aligned). The same as the address-space cast, without the cast's
+// test for a null pointer, which the compiler cannot drop for these pointers.
+__device__ __forceinline__ unsigned lds_offset(const void* p) {
+    return (unsigned)(uintptr_t)p;
+}
+
 // 16-byte global -> LDS copy (global_load_lds_dwordx4). Lane i of the wave writes
 // LDS bytes [dst + 16*i, dst + 16*i + 16); dst must be the same for the whole wave.
 // NT marks the load non-temporal: for bytes no other workgroup reads, so the caches do
@@ -108,8 +115,7 @@ __device__ __forceinline__ void load16_to_lds(const uint16_t* src, char* dst) {
     // copies and reads themselves (barrier_vmcnt); hidden copies can only make the
     // compiler's own vmcnt waits for other loads stricter, never looser.
     // M0 holds the wave's LDS base; lane i writes bytes [16 i, 16 i + 16) above it.
-    const unsigned lds = __builtin_amdgcn_readfirstlane(
-        (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)dst);
+    const unsigned lds = __builtin_amdgcn_readfirstlane(lds_offset(dst));
     // M0 is clobbered on purpose: nothing else in these kernels keeps a value in it.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
@@ -146,8 +152,7 @@ __device__ __forceinline__ uint64_t uniform_u64(uint64_t a) {
 // instructions. base must be the same for the whole wave.
 template <bool NT = false>
 __device__ __forceinline__ void load16_to_lds_sbase(const void* base, unsigned voff, char* dst) {
-    const unsigned lds = __builtin_amdgcn_readfirstlane(
-        (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)dst);
+    const unsigned lds = __builtin_amdgcn_readfirstlane(lds_offset(dst));
     const uint64_t sb = uniform_u64((uint64_t)(uintptr_t)base);
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
