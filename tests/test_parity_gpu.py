@@ -475,6 +475,48 @@ def test_dense_tensors_of_2_pow_31_elements():
     assert middle_batches_match_first(out)
 
 
+def test_prefix_tensors_of_2_pow_31_elements():
+    """Prefix attention, B=128 Nq=4096 Np=1024 H=32 D=128: Q, the current keys and values
+    and the output hold 2^31 elements each, the cached ones 2^29; checked as the dense
+    case above."""
+    B, Nq, Np, H, D = 128, 4096, 1024, 32, 128
+    need_free_gib(28)
+    say(f"prefix B{B} Nq{Nq} Np{Np} H{H} D{D}: 2^31 elements per current tensor")
+    (q, kc, vc), first, last = batched_copies((1, Nq, H, D), B, (1860, 1861, 1862),
+                                              (1870, 1871, 1872), (1.0, 1.0, 1.0))
+    (kp, vp), pfirst, plast = batched_copies((1, Np, H, D), B, (1863, 1864), (1873, 1874),
+                                             (1.0, 1.0))
+    out = attn.prefix(q, kp, vp, kc, vc)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(1880).choice(Nq * H, 512, replace=False))
+    for b, cur, pre in ((0, first, pfirst), (B - 1, last, plast)):
+        got = host(out[b]).reshape(-1, D)[rows]
+        ref = oracle.attention_rows(cur[0], pre[0], pre[1], cur[1], cur[2], rows=rows)
+        say(f"prefix 2^31 batch {b}: {assert_accepted(got, ref, f'prefix 2^31 batch {b}')}")
+    assert middle_batches_match_first(out)
+
+
+def test_block_causal_tensors_of_2_pow_31_elements():
+    """Block-causal attention, B=128 N=4096 H=32 D=128 with the image ids of the
+    block-causal workload (shared by the batch): 2^31 elements per tensor; checked as
+    the dense case above."""
+    B, N, H, D = 128, 4096, 32, 128
+    need_free_gib(24)
+    say(f"block-causal B{B} N{N} H{H} D{D}: 2^31 elements per tensor")
+    ids = synth.workload("block_causal_b1_n4096_h32_d128").image_ids()
+    (q, k, v), first, last = batched_copies((1, N, H, D), B, (1890, 1891, 1892),
+                                            (1895, 1896, 1897), (1.0, 1.0, 1.0))
+    out = attn.block_causal(q, k, v, torch.from_numpy(ids).cuda())
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(1899).choice(N * H, 512, replace=False))
+    for b, src in ((0, first), (B - 1, last)):
+        got = host(out[b]).reshape(-1, D)[rows]
+        ref = oracle.block_causal_rows(*src, ids, rows=rows)
+        say(f"block-causal 2^31 batch {b}: "
+            f"{assert_accepted(got, ref, f'block-causal 2^31 batch {b}')}")
+    assert middle_batches_match_first(out)
+
+
 def test_na3d_tensors_of_2_pow_31_elements():
     """B=64 T=8 Y=64 X=64 H=16 D=64, window 3x7x7: 2^31 elements per tensor, checked as
     the dense case above."""
