@@ -325,17 +325,25 @@ void attn_na3d_kernel(NaParams p) {
     // it puts none for the Q registers inside the loop, where the hardware count would
     // also take in the block copies just issued and expose their latency on every step.
     __builtin_amdgcn_s_waitcnt((0) | (0 << 14) | (7 << 4) | (15 << 8));  // vmcnt(0)
+    // The loop is unrolled over the ring's slots, so each block's slot is a constant and
+    // the LDS reads take it in their immediate offsets.
     int tt = tu0, yy = yu0;  // the block computed
-    for (int i = 0; i < nblocks; ++i) {
-        barrier_tiles_left<AHEAD - 1>(nblocks - 1 - i);
-        if (i + AHEAD < nblocks) issue_next((i + AHEAD) % NSLOT);  // the slot block i-1 left
-        if (active && yy < wv1 && yy + RPB > wv0 && tt >= tw0 && tt < tw0 + p.kt)
-            compute(kslot(i % NSLOT), vslot(i % NSLOT), yy, yy < wc0 || yy + RPB > wc1);
-        yy += RPB;
-        if (yy == yend) {
-            yy = yu0;
-            ++tt;
-        }
+    for (int i0 = 0; i0 < nblocks; i0 += NSLOT) {
+        static_for<NSLOT>([&](auto jc) {
+            constexpr int J = decltype(jc)::value;
+            const int i = i0 + J;
+            if (i < nblocks) {
+                barrier_tiles_left<AHEAD - 1>(nblocks - 1 - i);
+                if (i + AHEAD < nblocks) issue_next((J + AHEAD) % NSLOT);  // block i-1's slot
+                if (active && yy < wv1 && yy + RPB > wv0 && tt >= tw0 && tt < tw0 + p.kt)
+                    compute(kslot(J), vslot(J), yy, yy < wc0 || yy + RPB > wc1);
+                yy += RPB;
+                if (yy == yend) {
+                    yy = yu0;
+                    ++tt;
+                }
+            }
+        });
     }
 
     // ---- epilogue
