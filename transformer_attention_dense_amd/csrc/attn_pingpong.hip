@@ -323,25 +323,43 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // Returns false when no key of the tile is visible to any row of the wave (every
     // key after the wave's last row, and no image id shared with the rows): the caller
     // then sets the probabilities to zero without computing them.
-    auto bc_mask = [&](int t0) __attribute__((always_inline)) {
-        const bool whole = t0 + BN <= kend;
-        bool full = whole && t0 + BN - 1 <= q0;
-        if (!full) {
-            const int nblk = (p.Nq + kMetaRows - 1) / kMetaRows;
-            // summaries of the tile's NB row blocks of 32 keys
-            int kmin = 0x7fffffff, kmax = -1;
-            bool uni = true;
+    // The classes of the wave's tiles u0 .. u0 + 63 (bit u - u0), one lane per tile from the
+    // row-block summaries: every key visible to every row (full), or none to any (hidden).
+    unsigned long long bc_full = 0, bc_hidden = 0;
+    int bc_u0 = 0;
+    auto bc_classify = [&](int u0) {
+        const int u = u0 + lane;
+        const int t0 = kbeg + u * BN;
+        bool full = false, hidden = false;
+        if (t0 < kend) {
+            const bool whole = t0 + BN <= kend;
+            full = whole && t0 + BN - 1 <= q0;
+            if (!full) {
+                const int nblk = (p.Nq + kMetaRows - 1) / kMetaRows;
+                // summaries of the tile's NB row blocks of 32 keys
+                int kmin = 0x7fffffff, kmax = -1;
+                bool uni = true;
 #pragma unroll
-            for (int kb = 0; kb < NB; ++kb) {
-                const int* km = p.meta + 4 * min(t0 / kMetaRows + kb, nblk - 1);
-                kmin = min(kmin, km[0]);
-                kmax = max(kmax, km[1]);
-                uni = uni && km[2] == 0 && km[0] == wq_id && km[1] == wq_id;
+                for (int kb = 0; kb < NB; ++kb) {
+                    const int* km = p.meta + 4 * min(t0 / kMetaRows + kb, nblk - 1);
+                    kmin = min(kmin, km[0]);
+                    kmax = max(kmax, km[1]);
+                    uni = uni && km[2] == 0 && km[0] == wq_id && km[1] == wq_id;
+                }
+                hidden = t0 > q0 + 31 && (wq_max < 0 || kmax < wq_id || kmin > wq_max);
+                if (!hidden && whole && wq_uniform) full = uni;
             }
-            if (t0 > q0 + 31 && (wq_max < 0 || kmax < wq_id || kmin > wq_max)) return false;
-            if (whole && wq_uniform) full = uni;
         }
-        if (full) return true;
+        bc_full = __builtin_amdgcn_ballot_w64(full);
+        bc_hidden = __builtin_amdgcn_ballot_w64(hidden);
+        bc_u0 = u0;
+    };
+    auto bc_mask = [&](int t0) __attribute__((always_inline)) {
+        const int u = (t0 - kbeg) / BN;
+        if (u - bc_u0 >= 64) bc_classify(u);
+        const unsigned long long bit = 1ull << (u - bc_u0);
+        if (bc_hidden & bit) return false;
+        if (bc_full & bit) return true;
         const int i = q0 + n;
 #pragma unroll
         for (int kb = 0; kb < NB; ++kb)
@@ -477,6 +495,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     issue_k(kbeg, 0);
     if (T > 1) issue_k(kbeg + BN, 1);
     issue_v(kbeg, 0);
+    if constexpr (BC) {
+        if (active) bc_classify(0);
+    }
     barrier_vmcnt<0>();
     {
         const int tsw = lds_swizzle<CPR>(n) ^ g;
