@@ -189,6 +189,12 @@ BC_CASES = [
      ids_from([("image", 200), ("image", 150), ("text", 3), ("image", 247)])),
     (1, 300, 2, 64, "large_and_negative_ids",
      np.array([-5] * 40 + [10 ** 6] * 100 + [-1] * 60 + [7] * 100, np.int32)),
+    # more than 64 key tiles: the last row blocks classify their tiles in two chunks, the
+    # second image crossing the chunk boundary at key 4096
+    (1, 4700, 2, 128, "more_than_64_tiles",
+     ids_from([("text", 100), ("image", 2100), ("text", 60), ("image", 2380), ("text", 60)])),
+    (1, 4700, 1, 64, "more_than_64_tiles_d64",
+     ids_from([("image", 3000), ("text", 40), ("image", 1600), ("text", 60)])),
 ]
 
 
