@@ -64,11 +64,13 @@ def test_dense_small_all_elements(B, Nq, Nk, H, D, splits, waves):
     assert_accepted(got, ref, f"dense {w.name} s{splits} w{waves}")
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("Np", [0, 1, 17, 64, 100])
 @pytest.mark.parametrize("splits,waves", [(0, 0), (1, 0), (4, 0), (1, 8), (2, 8)])
-def test_prefix_small_all_elements(Np, splits, waves):
-    B, Nq, H, D = 2, 77, 3, 128
-    say(f"prefix Np{Np} splits{splits} waves{waves}")
+def test_prefix_small_all_elements(Np, splits, waves, D):
+    """Every element; with 8 waves at D = 64 the first 128-key tile holds both segments."""
+    B, Nq, H = 2, 77, 3
+    say(f"prefix Np{Np} D{D} splits{splits} waves{waves}")
     w = synth.small("prefix", B, Nq, H, D, 400 + Np, Np=Np, sigma_qk=2.0)
     q, kp, vp, kc, vc = w.tensors()
     ref = oracle.prefix_attention(q, kp, vp, kc, vc)
@@ -82,7 +84,7 @@ def test_prefix_small_all_elements(Np, splits, waves):
     else:
         got = (run_ex(q, kp, vp, kc, vc, splits=splits, waves=waves) if Np
                else run_ex(q, kc, vc, splits=splits, waves=waves))
-    assert_accepted(got, ref, f"prefix Np{Np}")
+    assert_accepted(got, ref, f"prefix Np{Np} D{D}")
 
 
 def test_cross_attention_unequal_lengths():
