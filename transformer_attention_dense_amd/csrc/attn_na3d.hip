@@ -325,23 +325,37 @@ void attn_na3d_kernel(NaParams p) {
     // it puts none for the Q registers inside the loop, where the hardware count would
     // also take in the block copies just issued and expose their latency on every step.
     __builtin_amdgcn_s_waitcnt((0) | (0 << 14) | (7 << 4) | (15 << 8));  // vmcnt(0)
+    // Which of the steps c0 .. c0 + 63 the wave computes (its windows reach the block's
+    // frame and rows) and which need the Y mask, one lane per step (bit i - c0).
+    unsigned long long st_act = 0, st_ym = 0;
+    int st_c0 = 0;
+    auto classify_steps = [&](int c0) {
+        const int i = c0 + lane;
+        bool act = false, ym = false;
+        if (active && i < nblocks) {
+            const int ti = tu0 + i / nbr, yi = yu0 + RPB * (i % nbr);
+            act = yi < wv1 && yi + RPB > wv0 && ti >= tw0 && ti < tw0 + p.kt;
+            ym = yi < wc0 || yi + RPB > wc1;
+        }
+        st_act = __builtin_amdgcn_ballot_w64(act);
+        st_ym = __builtin_amdgcn_ballot_w64(ym);
+        st_c0 = c0;
+    };
     // The loop is unrolled over the ring's slots, so each block's slot is a constant and
     // the LDS reads take it in their immediate offsets.
-    int tt = tu0, yy = yu0;  // the block computed
+    int yy = yu0;  // first row of the block computed
     for (int i0 = 0; i0 < nblocks; i0 += NSLOT) {
+        if ((i0 & 63) == 0) classify_steps(i0);  // NSLOT divides 64
         static_for<NSLOT>([&](auto jc) {
             constexpr int J = decltype(jc)::value;
             const int i = i0 + J;
             if (i < nblocks) {
                 barrier_tiles_left<AHEAD - 1>(nblocks - 1 - i);
                 if (i + AHEAD < nblocks) issue_next((J + AHEAD) % NSLOT);  // block i-1's slot
-                if (active && yy < wv1 && yy + RPB > wv0 && tt >= tw0 && tt < tw0 + p.kt)
-                    compute(kslot(J), vslot(J), yy, yy < wc0 || yy + RPB > wc1);
+                const unsigned long long bit = 1ull << (i - st_c0);
+                if (st_act & bit) compute(kslot(J), vslot(J), yy, (st_ym & bit) != 0);
                 yy += RPB;
-                if (yy == yend) {
-                    yy = yu0;
-                    ++tt;
-                }
+                if (yy == yend) yy = yu0;
             }
         });
     }
