@@ -171,7 +171,10 @@ int attn_plan(int B, int Nq, int Nk, int H, int D, int num_splits, int waves, in
  * HIP call). Any output pointer may be NULL. Returns ATTN_OK or the size/window error
  * attn_na3d would return.
  *   query_cols: positions on X of a wavefront's query tile (16, 8 or 4; the tile is
- *               32 / query_cols rows y by query_cols positions), chosen per window
+ *               32 / query_cols rows y by query_cols positions), chosen per window with
+ *               its key blocks of 32 keys (32 positions of one row for 16; 16 positions
+ *               of two rows for 8; for 4, 16 positions of two rows or, when kx <= 5 and
+ *               8 * X * H * D < 2^32, 8 positions of four rows)
  *   workgroups: workgroups of the kernel (four wavefronts each: 1, 2 or 4 frames by 4, 2
  *               or 1 row tiles, whichever walks the fewest key blocks)
  */

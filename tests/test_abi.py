@@ -239,34 +239,34 @@ def test_python_na3d_validates_before_the_library():
         attn.na3d(x[0], x[0], x[0], (1, 1, 1))
 
 
-@pytest.mark.parametrize("window,cols", [((3, 7, 7), 8), ((3, 5, 5), 8), ((11, 11, 11), 4),
-                                         ((1, 1, 17), 16), ((1, 3, 13), 16), ((1, 7, 13), 4),
-                                         ((1, 1, 15), 16),
-                                         ((1, 9, 9), 8)])
-def test_na3d_plan_picks_a_tile_that_holds_the_window(window, cols):
-    """A wave's query tile is 32 / c rows by c positions; its key blocks hold 32 positions
-    of one row (c = 16) or 16 positions of two rows (c = 8, 4), so the X windows of the c
-    positions, c - 1 + kx positions wide, must fit; among those the fewest keys per query
-    and t' ((32 / c + ky - 1) rows of the block width) wins."""
+@pytest.mark.parametrize("window,cols,width", [
+    ((3, 7, 7), 8, 16), ((3, 5, 5), 4, 8), ((11, 11, 11), 4, 16), ((1, 1, 17), 16, 32),
+    ((1, 3, 13), 16, 32), ((1, 7, 13), 4, 16), ((1, 1, 15), 16, 32), ((1, 9, 9), 8, 16),
+    ((1, 5, 3), 4, 8), ((1, 3, 5), 8, 16)])
+def test_na3d_plan_picks_a_tile_that_holds_the_window(window, cols, width):
+    """A wave's query tile is 32 / c rows by c positions; its key blocks hold 32 keys: 32
+    positions of one row (c = 16), 16 positions of two rows (c = 8, 4) or 8 positions of four
+    rows (c = 4), so the X windows of the c positions, c - 1 + kx positions wide, must fit
+    the block width; among those the fewest blocks per query and t' (32 / c + ky - 1 rows
+    in blocks of 32 / width rows) wins, ties to the tile listed first (1x3x5: 4x8 queries
+    over 16-position blocks and 8x4 queries over 8-position blocks both take three blocks)."""
     kt, ky, kx = window
     B, T, Y, X, H = 2, 11, 37, 45, 3
     plan = attn.attn_na3d_plan(B, T, Y, X, H, 64, kt, ky, kx)
     c = plan["query_cols"]
     assert c == cols
-    width = 32 if c == 16 else 16
     assert c - 1 + kx <= width
-    rows = 32 // c
-    assert plan["workgroups"] == na3d_grid(B, T, Y, X, H, window, c)
+    assert plan["workgroups"] == na3d_grid(B, T, Y, X, H, window, c, width)
 
 
-def na3d_grid(B, T, Y, X, H, window, c):
+def na3d_grid(B, T, Y, X, H, window, c, width):
     """Four waves per workgroup, arranged as wt frames t by 4 / wt tiles of 32 / c rows,
     wt in (1, 2, 4) walking the fewest key blocks: the union of the waves' windows, kt + wt - 1
     frames times blocks of 32 / width rows over the union of their Y windows (ties to the
     larger wt)."""
     kt, ky, _ = window
     rows = 32 // c
-    rpb = 32 // (32 if c == 16 else 16)
+    rpb = 32 // width
     best = None
     for wt in (1, 2, 4):
         steps = min(T, kt + wt - 1) * -(-min(Y, 4 // wt * rows + ky - 1) // rpb)
@@ -279,14 +279,17 @@ def na3d_grid(B, T, Y, X, H, window, c):
 def test_na3d_plan_arranges_waves_where_windows_overlap_most():
     """The pages' four neighborhood volumes: 3x7x7 on 64x64 or 32x32 walks 28 blocks with
     two frames by two row tiles (30 with four frames, 33 with four row tiles); 11x11x11 on
-    32x32 126 with four frames (156, 176); 3x5x5 on 64x64 24 with four frames (24, 30)."""
-    for (T, Y, X, H, win, wt) in [(8, 64, 64, 16, (3, 7, 7), 2), (8, 32, 32, 32, (3, 7, 7), 2),
-                                  (16, 32, 32, 4, (11, 11, 11), 4), (8, 64, 64, 8, (3, 5, 5), 4)]:
+    32x32 126 with four frames (156, 176); 3x5x5 on 64x64, 8x4 query tiles over blocks of
+    four rows, 18 with four frames (20, 27)."""
+    for (T, Y, X, H, win, wt, width) in [(8, 64, 64, 16, (3, 7, 7), 2, 16),
+                                         (8, 32, 32, 32, (3, 7, 7), 2, 16),
+                                         (16, 32, 32, 4, (11, 11, 11), 4, 16),
+                                         (8, 64, 64, 8, (3, 5, 5), 4, 8)]:
         plan = attn.attn_na3d_plan(1, T, Y, X, H, 64, *win)
         c = plan["query_cols"]
         rows = 32 // c
         assert plan["workgroups"] == -(-T // wt) * -(-Y // (4 // wt * rows)) * -(-X // c) * H
-        assert plan["workgroups"] == na3d_grid(1, T, Y, X, H, win, c)
+        assert plan["workgroups"] == na3d_grid(1, T, Y, X, H, win, c, width)
 
 
 def test_na3d_plan_errors_match_the_call():

@@ -392,6 +392,12 @@ NA_CASES = [
     (1, 2, 9, 20, 3, (1, 3, 5)),     # [4x8 1x4] the last key block's second row past the Y axis
     (1, 3, 3, 3, 4, (3, 3, 3)),      # [4x8 4x1] the window covers the volume
     (1, 2, 4, 97, 4, (1, 3, 9)),     # [4x8 1x4] 13 strips, the last one query wide
+    # 8x4 query tiles over key blocks of four rows of 8 positions (kx <= 5); the last
+    # block of a frame reaches rows past the Y axis
+    (1, 3, 13, 22, 2, (3, 5, 5)),    # [8x4] ragged rows and strips
+    (2, 2, 19, 9, 3, (1, 7, 3)),     # [8x4] two batches, a one-query strip
+    (1, 4, 10, 30, 2, (3, 9, 5)),    # [8x4] the Y window nearly the axis
+    (1, 5, 7, 5, 2, (5, 5, 5)),      # [8x4] the X window covers the axis
 ]
 
 

@@ -53,6 +53,7 @@ struct NaParams {
     int kt, ky, kx;
     // set by na3d_configure: a wave's query tile (32 / qb rows y x qb positions on X)
     int qb;       // 16, 8 or 4
+    int kw;       // positions on X of a key block (32, 16 or 8; 32 / kw rows)
     int strips;   // ceil(X / qb): strips of qb positions on the X axis
     int wt;       // frames t of a workgroup (1, 2 or 4), each with 4 / wt tiles of rows y
     int yblocks;  // blocks of rows y of a workgroup: ceil(Y / (4 / wt * 32 / qb))

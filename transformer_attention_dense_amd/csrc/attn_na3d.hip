@@ -10,8 +10,8 @@
 // frames t (4, 2 or 1 tiles of QA rows each), arranged where their windows overlap most. Every
 // (t', y') row of a query's window is a run of consecutive positions on X, and the X
 // windows of the QB positions lie in the KW positions starting at the window of the first
-// one (KW = 32 for QB = 16, else 16; kx <= KW - QB + 1), so a key block of 32 keys holds
-// KW positions of 32 / KW rows. The workgroup walks the union of its waves' Y windows for
+// one (KW = 32 for QB = 16, 16 for QB = 8, 16 or 8 for QB = 4; kx <= KW - QB + 1), so a key
+// block of 32 keys holds KW positions of 32 / KW rows. The workgroup walks the union of its waves' Y windows for
 // each t' of the union of their T windows as such blocks, streamed through a four-slot LDS ring
 // exactly like the dense kernels stream key tiles; each block is copied once and used by
 // every wave whose rows' windows reach its rows:
@@ -93,21 +93,23 @@ __device__ __forceinline__ void na_decode(const NaParams& p, int& b, int& t, int
 
 // Query tile of a wave: QA rows y x QB positions on X (32 queries). A key block is RPB
 // rows of KW positions on X (32 keys), the X windows of the QB positions lying in the KW
-// positions from the window of the first one (so kx <= KW - QB + 1).
-template <int QB>
+// positions from the window of the first one (so kx <= KW - QB + 1). Register r of a lane
+// holds key 8 (r / 4) + 4 g + r % 4 of the block, so row hr of the block is registers
+// 16 / RPB * hr .. 16 / RPB * (hr + 1) - 1.
+template <int QB, int KW_>
 struct NaTile {
     static constexpr int QA = 32 / QB;
-    static constexpr int KW = QB == 16 ? 32 : 16;
+    static constexpr int KW = KW_;
     static constexpr int RPB = 32 / KW;
     static constexpr int max_kx = KW - QB + 1;
 };
 
 // Four waves per SIMD (at most 128 VGPRs): the kernel is latency bound, and above 128
 // registers the compiler keeps the MFMA accumulators in AGPRs and copies them around.
-template <int QB>
+template <int QB, int KW_>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
 void attn_na3d_kernel(NaParams p) {
-    using Tile = NaTile<QB>;
+    using Tile = NaTile<QB, KW_>;
     constexpr int QA = Tile::QA, KW = Tile::KW, RPB = Tile::RPB;
     constexpr int D = 64;
     constexpr int KS = D / 16;       // MFMA k-steps over the head dim
@@ -182,6 +184,7 @@ void attn_na3d_kernel(NaParams p) {
     // holding logical chunk (tid % CPR) ^ swizzle(j). ld_off1 reads the block's first row
     // in place of its second, for a last block whose second row is past the axis.
     unsigned ld_off, ld_off1;
+    const int ld_row = (tid / CPR) / KW;  // the lane's row of the block
     {
         const int j = tid / CPR;
         const int xk = min(xa + j % KW, X - 1);
@@ -202,7 +205,11 @@ void attn_na3d_kernel(NaParams p) {
     int cp_t = tu0, cp_y = yu0;                          // next block to copy
     long cp_rb = bh0 + ((long)tu0 * Y + yu0) * rowb;
     auto issue_next = [&](int slot) {
-        const unsigned off = (RPB == 1 || cp_y + 1 < Y) ? ld_off : ld_off1;
+        unsigned off;
+        if constexpr (RPB <= 2)
+            off = (RPB == 1 || cp_y + 1 < Y) ? ld_off : ld_off1;
+        else  // rows past the axis read its last row (never visible)
+            off = ld_off1 + (unsigned)min(ld_row, Y - 1 - cp_y) * (unsigned)rowb;
         load16_to_lds_sbase(kbase + cp_rb, off, kslot(slot) + wave * kWave * 16);
         load16_to_lds_sbase(vbase + cp_rb, off, vslot(slot) + wave * kWave * 16);
         cp_y += RPB;
@@ -271,7 +278,7 @@ void attn_na3d_kernel(NaParams p) {
             for (int hr = 0; hr < RPB; ++hr) {
                 const float ym = (yy + hr >= ys_q && yy + hr < ys_q + p.ky) ? 0.f : -INFINITY;
 #pragma unroll
-                for (int r = 8 * hr; r < (RPB == 2 ? 8 * hr + 8 : 16); ++r) s[r] += ym;
+                for (int r = 16 / RPB * hr; r < 16 / RPB * (hr + 1); ++r) s[r] += ym;
             }
         }
         // ---- online softmax: running maximum raised only when a row's block maximum
@@ -377,24 +384,32 @@ void attn_na3d_kernel(NaParams p) {
 
 }  // namespace
 
-// Picks the wave tile whose key blocks cover a query's window with the fewest keys per
-// t' ((QA + ky - 1) rows of KW positions), among those whose blocks hold the X windows.
+// Picks the wave tile and key block whose blocks cover a query's window with the fewest
+// blocks per t' (QA + ky - 1 rows in blocks of 32 / KW rows), among those whose blocks hold
+// the X windows; ties go to the option listed first. Blocks of four rows of 8 positions
+// suit narrow windows (kx <= 5: 3x5x5 walks 18 blocks per workgroup instead of 24).
 void na3d_configure(NaParams& p) {
     struct Opt { int qb, qa, kw, max_kx; };
-    const Opt opts[] = {{16, NaTile<16>::QA, NaTile<16>::KW, NaTile<16>::max_kx},
-                        {8, NaTile<8>::QA, NaTile<8>::KW, NaTile<8>::max_kx},
-                        {4, NaTile<4>::QA, NaTile<4>::KW, NaTile<4>::max_kx}};
+    const Opt opts[] = {{16, NaTile<16, 32>::QA, 32, NaTile<16, 32>::max_kx},
+                        {8, NaTile<8, 16>::QA, 16, NaTile<8, 16>::max_kx},
+                        {4, NaTile<4, 16>::QA, 16, NaTile<4, 16>::max_kx},
+                        {4, NaTile<4, 8>::QA, 8, NaTile<4, 8>::max_kx}};
     long best = -1;
     p.qb = 0;
+    p.kw = 0;
     p.strips = p.yblocks = 0;  // no tile holds the window: nothing to launch
     p.wt = 1;
     int qa = 0, rpb = 0;
     for (const Opt& o : opts) {
         if (p.kx > o.max_kx) continue;
-        const long cost = (long)(o.qa + p.ky - 1) * o.kw;
+        // four-row blocks: a lane's byte offset to its row (at most three rows) in 32 bits
+        if (o.kw == 8 && 8LL * p.X * p.H * 64 >= (1LL << 32)) continue;
+        const int orpb = 32 / o.kw;
+        const long cost = (long)((o.qa + p.ky - 1 + orpb - 1) / orpb) * 32;
         if (best < 0 || cost < best) {
             best = cost;
             p.qb = o.qb;
+            p.kw = o.kw;
             qa = o.qa;
             rpb = 32 / o.kw;
         }
@@ -444,10 +459,11 @@ long long na3d_workgroups(const NaParams& p) {
 
 hipError_t launch_na3d(const NaParams& p, hipStream_t stream) {
     const dim3 grid((unsigned)na3d_workgroups(p)), block(kNaWaves * kWave);
-    switch (p.qb) {
-        case 16: hipLaunchKernelGGL(attn_na3d_kernel<16>, grid, block, 0, stream, p); break;
-        case 8: hipLaunchKernelGGL(attn_na3d_kernel<8>, grid, block, 0, stream, p); break;
-        case 4: hipLaunchKernelGGL(attn_na3d_kernel<4>, grid, block, 0, stream, p); break;
+    switch (p.qb * 100 + p.kw) {
+        case 1632: hipLaunchKernelGGL((attn_na3d_kernel<16, 32>), grid, block, 0, stream, p); break;
+        case 816: hipLaunchKernelGGL((attn_na3d_kernel<8, 16>), grid, block, 0, stream, p); break;
+        case 416: hipLaunchKernelGGL((attn_na3d_kernel<4, 16>), grid, block, 0, stream, p); break;
+        case 408: hipLaunchKernelGGL((attn_na3d_kernel<4, 8>), grid, block, 0, stream, p); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
