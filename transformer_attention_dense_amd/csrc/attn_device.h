@@ -150,9 +150,10 @@ __device__ __forceinline__ uint64_t uniform_u64(uint64_t a) {
 // The same copy with a wave-uniform base address and a per-lane 32-bit byte offset:
 // the load adds them itself (scalar-base form), so issuing it takes no vector
 // instructions. base must be the same for the whole wave.
+// lds: the wave's LDS byte address (uniform), as lds_offset() gives it.
 template <bool NT = false>
-__device__ __forceinline__ void load16_to_lds_sbase(const void* base, unsigned voff, char* dst) {
-    const unsigned lds = __builtin_amdgcn_readfirstlane(lds_offset(dst));
+__device__ __forceinline__ void load16_to_lds_sbase_at(const void* base, unsigned voff,
+                                                       unsigned lds) {
     const uint64_t sb = uniform_u64((uint64_t)(uintptr_t)base);
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
@@ -173,6 +174,11 @@ __device__ __forceinline__ void load16_to_lds_sbase(const void* base, unsigned v
             : "v"(voff), "s"(sb), "s"(lds)
             : "memory", "m0");
 #pragma clang diagnostic pop
+}
+
+template <bool NT = false>
+__device__ __forceinline__ void load16_to_lds_sbase(const void* base, unsigned voff, char* dst) {
+    load16_to_lds_sbase_at<NT>(base, voff, __builtin_amdgcn_readfirstlane(lds_offset(dst)));
 }
 
 // A pointer that is the same for the whole wave, kept in scalar registers.

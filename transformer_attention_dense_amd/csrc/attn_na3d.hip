@@ -202,22 +202,32 @@ void attn_na3d_kernel(NaParams p) {
     const long rowb = (long)X * HD * 2;  // bytes per row y of one frame
     const long bh0 = ((long)b * p.T * Y * X * HD + (long)h * D) * 2;
     const int yend = yu0 + nbr * RPB;
-    int cp_t = tu0, cp_y = yu0;                          // next block to copy
-    long cp_rb = bh0 + ((long)tu0 * Y + yu0) * rowb;
+    const long frame_step = (long)(Y - nbr * RPB) * rowb;  // from a frame's last block
+    int cp_y = yu0;                                          // next block to copy
+    const char* cp_k = kbase + bh0 + ((long)tu0 * Y + yu0) * rowb;
+    const char* cp_v = vbase + bh0 + ((long)tu0 * Y + yu0) * rowb;
+    // the wave's LDS addresses in each slot, once
+    unsigned lds_k[NSLOT], lds_v[NSLOT];
+#pragma unroll
+    for (int j = 0; j < NSLOT; ++j) {
+        lds_k[j] = __builtin_amdgcn_readfirstlane(lds_offset(kslot(j) + wave * kWave * 16));
+        lds_v[j] = __builtin_amdgcn_readfirstlane(lds_offset(vslot(j) + wave * kWave * 16));
+    }
     auto issue_next = [&](int slot) {
         unsigned off;
         if constexpr (RPB <= 2)
             off = (RPB == 1 || cp_y + 1 < Y) ? ld_off : ld_off1;
         else  // rows past the axis read its last row (never visible)
             off = ld_off1 + (unsigned)min(ld_row, Y - 1 - cp_y) * (unsigned)rowb;
-        load16_to_lds_sbase(kbase + cp_rb, off, kslot(slot) + wave * kWave * 16);
-        load16_to_lds_sbase(vbase + cp_rb, off, vslot(slot) + wave * kWave * 16);
+        load16_to_lds_sbase_at(cp_k, off, lds_k[slot]);
+        load16_to_lds_sbase_at(cp_v, off, lds_v[slot]);
         cp_y += RPB;
-        cp_rb += RPB * rowb;
-        if (cp_y == yend) {
+        cp_k += RPB * rowb;
+        cp_v += RPB * rowb;
+        if (cp_y == yend) {  // the next frame's first block
             cp_y = yu0;
-            ++cp_t;
-            cp_rb = bh0 + ((long)cp_t * Y + yu0) * rowb;
+            cp_k += frame_step;
+            cp_v += frame_step;
         }
     };
 
