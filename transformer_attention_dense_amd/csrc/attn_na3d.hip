@@ -20,8 +20,9 @@
 //     fixed for the workgroup; positions past the end of the X axis are clamped and never
 //     visible), three blocks ahead of their use;
 //   * S^T = K Q^T with 32x32x16 BF16 MFMAs (S in FP32), accumulated onto a per-lane
-//     0/-inf mask of the keys outside its query's X window; keys of rows outside its Y
-//     window get -inf added where the block is not inside every Y window of the wave;
+//     0/-inf mask of the keys outside its query's X window; where the block is not inside
+//     every Y window of the wave, the rows outside a query's window are left out of its
+//     maximum and its exponentials of them get a reference of +inf (so they are 0);
 //   * online softmax in the exp2 domain (scale 1, so c = log2 e), P rounded to BF16;
 //   * O^T += V^T P^T with the V operand read transposed from LDS (ds_read_b64_tr_b16).
 #include <hip/hip_runtime.h>
@@ -274,7 +275,7 @@ void attn_na3d_kernel(NaParams p) {
     }
 
     // One block; ymask when some of its rows lie outside the Y window of some query of
-    // the wave (those rows' keys get -inf for that query). ymask is uniform.
+    // the wave (those rows' keys are hidden from that query). ymask is uniform.
     auto compute = [&](const char* kt_lds, const char* vt_lds, int yy, bool ymask) {
         // ---- S^T = K Q^T, onto the X window mask
         f32x16 s = xm;
@@ -283,19 +284,31 @@ void attn_na3d_kernel(NaParams p) {
             const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt_lds + koff[ks]);
             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s, 0, 0, 0);
         }
+        // ---- online softmax: running maximum raised only when a row's block maximum
+        // exceeds it by more than 2^kRescaleLog2 in the exp2 domain. Where rows of the
+        // block lie outside the query's Y window (ymask), they are left out of the maximum
+        // and their exponentials get a reference of +inf (so they are 0), instead of -inf
+        // added to each of their scores.
+        constexpr int RR = 16 / RPB;  // registers per row of the block
+        float mx;
+        bool hid[RPB];
         if (ymask) {
+            mx = -INFINITY;
 #pragma unroll
             for (int hr = 0; hr < RPB; ++hr) {
-                const float ym = (yy + hr >= ys_q && yy + hr < ys_q + p.ky) ? 0.f : -INFINITY;
+                hid[hr] = !(yy + hr >= ys_q && yy + hr < ys_q + p.ky);
+                float m = s[RR * hr];
 #pragma unroll
-                for (int r = 16 / RPB * hr; r < 16 / RPB * (hr + 1); ++r) s[r] += ym;
+                for (int r = RR * hr + 1; r < RR * (hr + 1); ++r) m = fmaxf(m, s[r]);
+                mx = fmaxf(mx, hid[hr] ? -INFINITY : m);
             }
-        }
-        // ---- online softmax: running maximum raised only when a row's block maximum
-        // exceeds it by more than 2^kRescaleLog2 in the exp2 domain
-        float mx = s[0];
+        } else {
 #pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+            for (int hr = 0; hr < RPB; ++hr) hid[hr] = false;
+            mx = s[0];
+#pragma unroll
+            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+        }
         mx = wave_swap_max(mx);
         const bool need = (mx - m_ref) * c > kRescaleLog2;
         if (__builtin_amdgcn_ballot_w64(need) != 0) {
@@ -308,12 +321,15 @@ void attn_na3d_kernel(NaParams p) {
         }
         // a query that has seen no key yet keeps m_ref = -inf; its scores are -inf too
         const float mc = (m_ref == -INFINITY) ? 0.f : m_ref * c;
+        float mcr[RPB];
+#pragma unroll
+        for (int hr = 0; hr < RPB; ++hr) mcr[hr] = hid[hr] ? INFINITY : mc;
         bf16x8 pf[2];
         static_for<NPAIR>([&](auto pc) {
             constexpr int pi = decltype(pc)::value;
             constexpr int tt2 = pi / 4, r = 8 * tt2 + 2 * (pi % 4);
-            const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -mc));
-            const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 1], c, -mc));
+            const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -mcr[r / RR]));
+            const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 1], c, -mcr[(r + 1) / RR]));
             const bf16x2 pk = {(__bf16)e0, (__bf16)e1};
             l_part = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, l_part, false);
             pf[tt2][r & 7] = pk[0];
